@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Benchmark of the InfLLM-V2 sparse-attention prefill path on one MI355X.
+
+One step = the whole sparse path for one attention layer over one 131072-token
+sequence (32 query heads, 2 KV heads, head_dim 128, |I| = 1 + 32 + 63 = 96
+blocks of 64 tokens, 32 needle blocks): compress_k (stage-1 keys, plus the
+coarse keys in approx mode) -> select_blocks (LSE pass, fused group-sum /
+max-pool pass, top-k) -> sparse_attn.  Inputs are resident in HBM before the
+timed region.  V is supplied in the transposed layout [h_kv, d, batch, n]
+that the attention kernel reads (the V projection can emit it directly).
+
+Prints one JSON line (see the keys below), with a roofline entry for the
+dominant kernel (sparse attention) measured with HIP events on the stream it
+runs on, and the fp64 oracle timed on a bounded sample as CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn prefill tokens/s @128K (32q/2kv,d128,|I|=96); % MFMA peak"
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def visible_keys(t, n_sel, B=64):
+    bt = t // B
+    return np.where(bt < n_sel, t + 1, (n_sel - 1) * B + (t % B) + 1)
+
+
+def algorithmic_work(n, h_q, h_kv, d=128, n_init=1, n_local=32, n_topk=63):
+    """Algorithmic flops / bytes of each stage for one prefill of length n
+    (no masked or padded work counted)."""
+    n_sel = n_init + n_local + n_topk
+    t = np.arange(n, dtype=np.int64)
+    bt = t // 64
+    scored = bt >= n_sel                      # rows with more candidates than n_topk
+    nv1 = np.clip((t - 31) // 16 + 1, 0, None)
+    nv2 = np.clip((t - 127) // 64 + 1, 0, None)
+    cand_windows = np.clip(4 * (bt - n_local) + 4 - max(0, 4 * n_init - 1), 0, None)
+    ncand = np.clip(bt - n_local - n_init + 1, 0, None)
+    w = {}
+    w["attn_flops"] = float(4 * d * h_q * visible_keys(t, n_sel).sum())
+    w["lse_exact_flops"] = float(2 * d * h_q * nv1[scored].sum())
+    w["lse_approx_flops"] = float(2 * d * h_q * nv2[scored].sum())
+    w["blocks_flops"] = float(2 * d * h_q * cand_windows[scored].sum())
+    w["topk_bytes"] = float(4 * h_kv * ncand[scored].sum() + 4 * h_kv * n * n_sel)
+    n1, n2 = (n - 32) // 16 + 1, (n - 128) // 64 + 1
+    w["compress_bytes"] = float(2 * h_kv * d * (n + n1))
+    w["compress2_bytes"] = float(2 * h_kv * d * (n + n2))
+    return w
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src):
+    """HBM bytes per launch from the committed PMC summary, if it was taken
+    on the current kernel source; None otherwise."""
+    f = os.path.join(ROOT, "profiles", "attn_kernel_128k_pmc.json")
+    if not os.path.exists(f):
+        return None
+    try:
+        rec = json.load(open(f))
+    except Exception:
+        return None
+    if rec.get("source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, n, h_q, h_kv, lse_mode, budget_s=15.0):
+    """The fp64 oracle on a bounded sample of the same workload: the full
+    stage-1 compression once, then whole rows (selection + attention) at
+    evenly spaced positions until the time budget is spent; the rate is
+    extrapolated to all n rows.  BLAS is limited to one thread."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle.reference as R
+    p = R.Params(lse_mode=lse_mode, round_kc=True)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        KC1 = R.compress_keys(inp.k, 32, 16, True)
+        KC2 = R.compress_keys(inp.k, 128, 64, True) if lse_mode == "approx" else None
+        Kf, Vf = R.as_f64(inp.k), R.as_f64(inp.v)
+        t_pre = time.perf_counter() - t0
+        rows = 0
+        t1 = time.perf_counter()
+        positions = np.linspace(0, n - 1, 64).astype(int)
+        order = np.random.Generator(np.random.PCG64(0)).permutation(positions)
+        for t in order:
+            t = int(t)
+            sel, _ = R.select_token(inp.q[t], t, KC1, KC2, h_q // h_kv, p)
+            R.attend_token(inp.q[t], t, Kf, Vf, sel, h_q // h_kv, p)
+            rows += 1
+            if time.perf_counter() - t1 > budget_s:
+                break
+        t_rows = time.perf_counter() - t1
+    per_row = t_rows / rows
+    value = n / (t_pre + n * per_row)
+    return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 oracle, 1 BLAS thread: stage-1 compression of all {n} tokens "
+                      f"({t_pre:.1f} s) + {rows} full rows (selection + attention) at spread "
+                      f"positions ({t_rows:.1f} s), extrapolated to {n} rows"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--seq", type=int, default=131072)
+    ap.add_argument("--lse", choices=["exact", "approx"], default="exact")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
+                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        sys.exit(2)
+
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    n, h_q, h_kv, d = args.seq, 32, 2, 128
+    print(f"[bench] generating inputs n={n}", file=sys.stderr, flush=True)
+    inp = D.make_prefill(3, n, h_q, h_kv, d, n_needles=32)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    vt = v.permute(1, 2, 0).contiguous().view(h_kv, d, 1, n)   # caller-side layout, outside the timed region
+    out = torch.empty_like(q)
+    cfg = P.SparseConfig(lse_mode=args.lse)
+    plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        plan.compress(k)
+        if ev is not None:
+            ev[1].record(stream)
+        plan.select(q)
+        if ev is not None:
+            ev[2].record(stream)
+        B.sparse_attn(q, k, vt, plan.cu_q, plan.used_q, plan.cu_k, plan.used_k, 1, n, n,
+                      plan.block_idx, cfg.n_init, cfg.n_local, cfg.scale(d), out, None, None,
+                      v_seq_stride=n)
+        if ev is not None:
+            ev[3].record(stream)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(args.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    ms_compress = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    ms_select = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    ms_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+
+    w = algorithmic_work(n, h_q, h_kv, d)
+    lse_flops = w["lse_exact_flops"] if args.lse == "exact" else w["lse_approx_flops"]
+    mfma_flops = w["attn_flops"] + lse_flops + w["blocks_flops"]
+    attn_tflops = w["attn_flops"] / (ms_attn * 1e-3) / 1e12
+    kernel_src = os.path.join(ROOT, "trainable_block_sparse_compress_amd", "csrc", "attention.hip")
+    traffic = traffic_from_profile(kernel_src)
+    res = {
+        "metric": METRIC,
+        "value": n / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 Q/K/V with 32 planted needle blocks",
+        "config": {"workload": f"sparse prefill, one layer, n={n}", "seq_len": n, "h_q": h_q,
+                   "h_kv": h_kv, "head_dim": d, "block_size": 64, "n_init": 1, "n_local": 32,
+                   "n_topk": 63, "lse": args.lse},
+        "mfma_frac_of_peak": mfma_flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        "ms_compress_k": ms_compress,
+        "ms_select_blocks": ms_select,
+        "ms_sparse_attn": ms_attn,
+        "roofline": {"bound": "mfma", "kernel": "attn_kernel (infllmv2_sparse_attn)",
+                     "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+    }
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(inp, n, h_q, h_kv, args.lse, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,214 @@
+/*
+ * infllmv2.h — C ABI of the InfLLM-V2 sparse-attention path on MI355X (gfx950).
+ *
+ * The path (switch pseudocode in the reading notes "论文阅读：InfLLM-V2",
+ * section "Dense-Sparse Switchable Attention"):
+ *
+ *   if seq_len <= threshold:  y = dense_attention(q, k, v)          -> infllmv2_dense_attn
+ *   else:
+ *     compressed keys (stage 1)                                    -> infllmv2_compress_k
+ *     scores, group sum, max pool, init ∪ local ∪ top-k            -> infllmv2_select_blocks
+ *     y = sparse attention over the selected blocks                -> infllmv2_sparse_attn
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates, frees or synchronises; it only enqueues kernels on
+ *    `stream` (a hipStream_t, NULL = the null stream).  Scratch memory is a
+ *    caller-provided `workspace`; passing workspace == NULL with a non-NULL
+ *    `workspace_bytes` only writes the required size and returns 0 without
+ *    touching the GPU.
+ *  - bf16 tensors are passed as void* (bfloat16 storage, 2 bytes each).
+ *  - Packed variable-length batches: sequence s's queries are rows
+ *    cu_seqlens_q[s] .. cu_seqlens_q[s] + len_q(s) - 1 of q/out, its keys rows
+ *    cu_seqlens_k[s] .. of k (and v).  len_q(s) = seqused_q[s] if seqused_q is
+ *    not NULL, else cu_seqlens_q[s+1] - cu_seqlens_q[s]; likewise len_k(s).
+ *    With seqused_* given, cu_seqlens_* needs only `batch` entries, and the
+ *    sequences may be any subset of a packed buffer (this is how the
+ *    dense/sparse switch hands one packed batch to both paths).
+ *  - Causality is bottom-right: query i of sequence s sits at position
+ *    len_k(s) - len_q(s) + i and sees keys 0 .. that position.  A decode step
+ *    is the same call with len_q = 1.
+ *  - Positions, blocks and compressed windows restart at each sequence.
+ *  - Per-sequence metadata (cu_seqlens, seqused, cu_c*) lives on the device
+ *    and is trusted: kernels clip every access to the row counts passed by
+ *    value (rows_q, rows_k, c_rows), so inconsistent metadata cannot make them
+ *    read or write outside the buffers, but it gives unspecified results.
+ *  - Supported shapes: head_dim = 128, block_size = 64, h_q = G * h_kv with
+ *    group size G in {1, 2, 4, 8, 16} (the kernels are tiled for G = 16, the
+ *    GQA group size the top168.com article, section 七 "技术实现的创新细节",
+ *    names as suited to block-sparse attention; smaller G is padded).
+ *  - Errors: every argument is validated on the host before any HIP call.
+ *    Returns INFLLMV2_OK or a negative code; infllmv2_last_error() gives a
+ *    thread-local message for the last failing call on the calling thread.
+ *    Calls are re-entrant; the library holds no global state besides that
+ *    message.
+ */
+#ifndef INFLLMV2_H
+#define INFLLMV2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define INFLLMV2_OK            0
+#define INFLLMV2_EINVAL       (-1)  /* inconsistent or out-of-range argument */
+#define INFLLMV2_EUNSUPPORTED (-2)  /* valid for the method, not implemented here */
+#define INFLLMV2_EWORKSPACE   (-3)  /* workspace missing or smaller than required */
+#define INFLLMV2_EHIP         (-4)  /* a HIP launch failed */
+
+/* Static description of an error code. */
+const char* infllmv2_strerror(int code);
+
+/* Thread-local detail of the last failing call on this thread ("" if none). */
+const char* infllmv2_last_error(void);
+
+/* Library version string. */
+const char* infllmv2_version(void);
+
+/*
+ * infllmv2_compress_k — stage 1 of the three-stage block representation:
+ * parameter-free mean pooling of the keys (top168.com article, section 三
+ * "块表示的三阶段压缩": kernel l_C1 = B/2, stride s_C1 = B/4; the coarse keys of the
+ * LSE approximation in section 四 use l_C2 = 4 l_C1, s_C2 = 4 s_C1).
+ *
+ *   k_cmp[g, cu_cmp[s] + j, :] = bf16( (1/kernel) * sum_{u < kernel} k[row(s, stride*j + u), g, :] )
+ *
+ * for every complete window j < N(len_k(s)) = (len_k - kernel) / stride + 1
+ * (0 when len_k < kernel).  The sum is exact (float64) and rounded once to
+ * bf16, to nearest even.
+ *
+ *   k          bf16 [rows_k, h_kv, head_dim]
+ *   cu_seqlens_k, seqused_k   key rows of each sequence (seqused_k nullable)
+ *   cu_cmp     int32 [batch]: first row of sequence s in k_cmp (caller computes
+ *              the offsets; N() above gives each sequence's count)
+ *   cmp_begin  int32 [batch] or NULL: windows j < cmp_begin[s] are left
+ *              untouched (incremental use in decode: only windows completed
+ *              since the last call are written)
+ *   max_new    with cmp_begin: at most this many windows are written per
+ *              sequence, starting at cmp_begin[s] (sizes the launch; a decode
+ *              step of one token completes at most one window); ignored
+ *              without cmp_begin
+ *   k_cmp      bf16 [h_kv, c_rows, head_dim]  (head-major)
+ *   kernel_size, stride  any positive pair; the path uses (32, 16) and (128, 64)
+ */
+int infllmv2_compress_k(const void* k, const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                        int32_t batch, int32_t max_seqlen_k, int64_t rows_k,
+                        int32_t h_kv, int32_t head_dim,
+                        int32_t kernel_size, int32_t stride,
+                        const int32_t* cu_cmp, const int32_t* cmp_begin, int32_t max_new,
+                        int64_t c_rows, void* k_cmp, void* stream);
+
+/*
+ * infllmv2_select_blocks — block scoring and selection (top168.com article,
+ * sections 三 and 四; section 七 for the union; reading notes section
+ * "先看一个具体例子" for the 1 + 32 + 63 = 96-block budget of 64 tokens).
+ *
+ * For every query row t of KV group g:
+ *   z[h, j]   = softmax_scale * q[t, h] . k_c1[g, j]           (windows visible
+ *               to t: stride*j + kernel - 1 <= position)
+ *   L[h]      = log sum_j exp z[h, j]   (exact: two-pass, k_c2 == NULL) or the
+ *               same log-sum-exp over the coarse keys k_c2 (approximation)
+ *   S[g, j]   = sum_{h in group g} exp(z[h, j] - L[h])       (group sum, fused
+ *               in the score kernel; only block maxima reach memory)
+ *   score[b]  = max_{j in 4b-1 .. 4b+3} S[g, j]              (max pool 5 / 4,
+ *               left pad 1: the stage-1 windows overlapping block b)
+ *   I(t, g)   = {0..n_init-1} ∪ {b_t-n_local+1..b_t} ∪ top-n_topk over the
+ *               remaining causal blocks n_init..b_t-n_local by (score desc,
+ *               block index asc); every causal block when there are no more
+ *               than n_topk candidates.
+ *
+ *   q          bf16 [rows_q, h_q, head_dim]
+ *   k_c1       bf16 [h_kv, c1_rows, head_dim] from infllmv2_compress_k(32, 16)
+ *   k_c2       bf16 [h_kv, c2_rows, head_dim] from infllmv2_compress_k(128, 64),
+ *              or NULL for the exact two-pass LSE
+ *   cu_c1, cu_c2   int32 [batch] first compressed row per sequence (cu_c2 may
+ *              be NULL iff k_c2 is NULL)
+ *   block_idx  int32 [h_kv, rows_q, n_init + n_local + n_topk] (written):
+ *              ascending block ids, -1 padded.  Rows of q outside every
+ *              sequence are not written.
+ *   workspace  >= *workspace_bytes as returned by a size query with the same
+ *              shape arguments (fp32 LSE and block scores)
+ *   Supported: (c1_kernel, c1_stride) = (32, 16), (c2_kernel, c2_stride) =
+ *   (128, 64), pool (5, 4, 1), n_init + n_local + n_topk >= 1 (>= 2 with
+ *   k_c2, so that every row that needs scores sees a coarse window), at most
+ *   8192 blocks per sequence.
+ */
+int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
+                           const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                           const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                           const int32_t* cu_c1, const int32_t* cu_c2,
+                           int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                           int64_t rows_q, int64_t c1_rows, int64_t c2_rows,
+                           int32_t h_q, int32_t h_kv, int32_t head_dim, int32_t block_size,
+                           int32_t n_init, int32_t n_local, int32_t n_topk,
+                           int32_t c1_kernel, int32_t c1_stride,
+                           int32_t c2_kernel, int32_t c2_stride,
+                           int32_t pool_kernel, int32_t pool_stride, int32_t pool_pad,
+                           float softmax_scale,
+                           void* workspace, size_t* workspace_bytes,
+                           int32_t* block_idx, void* stream);
+
+/*
+ * infllmv2_sparse_attn — block-sparse causal attention, the single output
+ * branch (reading notes section "对齐计算图"; top168.com article section 七:
+ * local blocks absorb the sliding window):
+ *
+ *   out[t, h] = sum_{u in T} softmax_u(softmax_scale * q[t, h] . k[u, g]) v[u, g],
+ *   T = {u <= position(t) : floor(u / 64) in init(t) ∪ local(t) ∪ block_idx[g, t, :]}
+ *
+ * with init(t) = {0..n_init-1} and local(t) = {b_t-n_local+1..b_t}.  Each
+ * row of block_idx is ascending; entries equal to -1, repeating the previous
+ * entry, or later than b_t are skipped.  The output of
+ * infllmv2_select_blocks can be passed as is, and any other ascending block
+ * list works with n_init = n_local = 0.  A row that attends no key gets
+ * out = 0 and lse = -inf.
+ *
+ *   q, out     bf16 [rows_q, h_q, head_dim]
+ *   k          bf16 [rows_k, h_kv, head_dim]
+ *   v          v_seq_stride == 0: bf16 [rows_k, h_kv, head_dim] (same rows as k;
+ *              the library transposes it into the workspace once per call);
+ *              v_seq_stride  > 0: bf16 [h_kv, head_dim, batch, v_seq_stride]
+ *              (a transposed cache: sequence s's key i at column i; the stride
+ *              must be a multiple of 64; columns past len_k(s) are never used)
+ *   block_idx  int32 [h_kv, rows_q, n_sel]
+ *   lse_out    float [h_q, rows_q] natural-log softmax normaliser, or NULL
+ *   workspace  size from a query with the same shape arguments (0 bytes when
+ *              v_seq_stride > 0)
+ */
+int infllmv2_sparse_attn(const void* q, const void* k, const void* v,
+                         const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                         const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                         int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                         int64_t rows_q, int64_t rows_k,
+                         int32_t h_q, int32_t h_kv, int32_t head_dim, int32_t block_size,
+                         const int32_t* block_idx, int32_t n_sel, int32_t n_init, int32_t n_local,
+                         float softmax_scale, int64_t v_seq_stride,
+                         void* out, float* lse_out,
+                         void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * infllmv2_dense_attn — plain causal attention over every key <= position,
+ * the path short sequences take (reading notes section "Dense-Sparse
+ * Switchable Attention"; dtcms.com article section 二.2.c: dense below a
+ * length threshold).  Same layouts, v conventions and workspace rule as
+ * infllmv2_sparse_attn.
+ */
+int infllmv2_dense_attn(const void* q, const void* k, const void* v,
+                        const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                        const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                        int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                        int64_t rows_q, int64_t rows_k,
+                        int32_t h_q, int32_t h_kv, int32_t head_dim,
+                        float softmax_scale, int64_t v_seq_stride,
+                        void* out, float* lse_out,
+                        void* workspace, size_t* workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INFLLMV2_H */

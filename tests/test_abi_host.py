@@ -1,0 +1,151 @@
+"""Host-only checks of the C ABI: the library loads, exports every symbol the
+header declares, validates arguments before any HIP call and answers
+workspace-size queries without touching a GPU.  No compute call is made."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from trainable_block_sparse_compress_amd import binding as B
+from trainable_block_sparse_compress_amd import pipeline as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "infllmv2.h")
+
+OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(infllmv2_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for n in ("infllmv2_compress_k", "infllmv2_select_blocks", "infllmv2_sparse_attn",
+              "infllmv2_dense_attn"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_and_version(lib):
+    assert B.version().startswith("infllmv2-gfx950")
+    for code in (OK, EINVAL, EUNSUP, EWS, -4):
+        assert lib.infllmv2_strerror(code)
+    assert lib.infllmv2_strerror(7) == b"unknown error"
+
+
+def _select(lib, **kw):
+    a = dict(q=None, k_c1=None, k_c2=None, cu_q=None, used_q=None, cu_k=None, used_k=None,
+             cu_c1=None, cu_c2=None, batch=1, max_q=4096, max_k=4096, rows_q=4096, c1_rows=255,
+             c2_rows=0, h_q=32, h_kv=2, d=128, B=64, n_init=1, n_local=32, n_topk=63, c1k=32,
+             c1s=16, c2k=128, c2s=64, pk=5, ps=4, pp=1, scale=0.088, ws=None, query=True, idx=None)
+    a.update(kw)
+    size = ctypes.c_size_t(0)
+    rc = lib.infllmv2_select_blocks(
+        a["q"], a["k_c1"], a["k_c2"], a["cu_q"], a["used_q"], a["cu_k"], a["used_k"], a["cu_c1"],
+        a["cu_c2"], a["batch"], a["max_q"], a["max_k"], a["rows_q"], a["c1_rows"], a["c2_rows"],
+        a["h_q"], a["h_kv"], a["d"], a["B"], a["n_init"], a["n_local"], a["n_topk"], a["c1k"],
+        a["c1s"], a["c2k"], a["c2s"], a["pk"], a["ps"], a["pp"], a["scale"], a["ws"],
+        ctypes.byref(size) if a["query"] else None, a["idx"], None)
+    return rc, size.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=64), EUNSUP),
+    (dict(B=128), EUNSUP),
+    (dict(h_q=31), EINVAL),
+    (dict(h_q=64, h_kv=2), EUNSUP),           # G = 32
+    (dict(c1k=64), EUNSUP),
+    (dict(pp=0), EUNSUP),
+    (dict(n_init=0, n_local=0, n_topk=0), EINVAL),
+    (dict(n_topk=-1), EINVAL),
+    (dict(scale=0.0), EINVAL),
+    (dict(scale=float("nan")), EINVAL),
+    (dict(batch=-1), EINVAL),
+    (dict(max_q=5000), EINVAL),               # queries longer than keys
+    (dict(max_k=64 * 8193, max_q=64), EUNSUP),  # more than 8192 blocks
+    (dict(k_c2=ctypes.c_void_p(16), n_init=1, n_local=0, n_topk=0), EINVAL),  # approx, |I|*64 < 128
+    (dict(k_c2=ctypes.c_void_p(16), c2k=256), EUNSUP),
+])
+def test_select_blocks_validation(lib, kw, code):
+    rc, _ = _select(lib, **kw)
+    assert rc == code
+    assert lib.infllmv2_last_error()
+
+
+def test_select_blocks_workspace_size(lib):
+    rows, h_q, h_kv, n = 131072, 32, 2, 131072
+    rc, size = _select(lib, max_q=n, max_k=n, rows_q=rows, h_q=h_q, h_kv=h_kv)
+    assert rc == OK
+    lse = h_q * rows * 4
+    bs_ld = ((n // 64 + 3) // 4) * 4
+    bs = h_kv * rows * bs_ld * 4
+    align = lambda x: (x + 255) // 256 * 256
+    assert size == align(lse) + align(bs)
+
+
+def test_select_blocks_missing_workspace(lib):
+    rc, _ = _select(lib, query=False, q=ctypes.c_void_p(16))
+    assert rc == EWS
+
+
+def test_attention_validation_and_workspace(lib):
+    size = ctypes.c_size_t(0)
+    rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 2, 100, 100, 200, 200,
+                                 32, 2, 128, 0.088, 0, None, None, None, ctypes.byref(size), None)
+    assert rc == OK and size.value == 2 * 128 * 2 * 128 * 2
+    rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
+                                 32, 2, 96, 0.088, 0, None, None, None, ctypes.byref(size), None)
+    assert rc == EUNSUP
+    rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
+                                 32, 2, 128, 0.088, 100, None, None, None, ctypes.byref(size), None)
+    assert rc == EINVAL  # v_seq_stride not a multiple of 64
+    rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
+                                 32, 2, 128, 0.088, 64, None, None, None, ctypes.byref(size), None)
+    assert rc == OK and size.value == 0
+    rc = lib.infllmv2_sparse_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
+                                  32, 2, 128, 64, None, 0, 1, 32, 0.088, 0, None, None, None,
+                                  ctypes.byref(size), None)
+    assert rc == EINVAL  # n_sel = 0
+    rc = lib.infllmv2_sparse_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
+                                  32, 2, 128, 32, None, 96, 1, 32, 0.088, 0, None, None, None,
+                                  ctypes.byref(size), None)
+    assert rc == EUNSUP  # block size 32
+
+
+def test_compress_validation(lib):
+    rc = lib.infllmv2_compress_k(None, None, None, 1, 100, 100, 2, 64, 32, 16, None, None, 0, 10,
+                                 None, None)
+    assert rc == EUNSUP
+    rc = lib.infllmv2_compress_k(None, None, None, 1, 100, 100, 2, 128, 0, 16, None, None, 0, 10,
+                                 None, None)
+    assert rc == EINVAL
+    rc = lib.infllmv2_compress_k(None, None, None, 1, 100, 100, 2, 128, 32, 16, None,
+                                 ctypes.c_void_p(16), 0, 10, None, None)
+    assert rc == EINVAL  # cmp_begin without max_new
+    rc = lib.infllmv2_compress_k(None, None, None, 1, 100, 100, 2, 128, 32, 16, None, None, 0, 10,
+                                 None, None)
+    assert rc == EINVAL  # null pointers with work to do
+    rc = lib.infllmv2_compress_k(None, None, None, 1, 20, 20, 2, 128, 32, 16, None, None, 0, 0,
+                                 None, None)
+    assert rc == OK  # no complete window: nothing to do
+
+
+def test_switch_partition_and_window_counts():
+    import oracle.reference as R
+    cfg = P.SparseConfig()
+    for n in (0, 31, 32, 100, 4096, 131072):
+        assert P.n_windows(n, *cfg.c1) == R.n_windows(n, 32, 16)
+        assert P.n_windows(n, *cfg.c2) == R.n_windows(n, 128, 64)
+    assert cfg.n_sel == 96

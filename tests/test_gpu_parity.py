@@ -1,0 +1,434 @@
+"""Parity of the HIP path (called through the C ABI) with the fp64 oracle.
+
+Bars: compressed keys bit-exact; block selection per the acceptance rule
+(exact match except inside the 1e-3 relative tie band around the k-th
+score); attention max-abs <= 2e-2 and relative RMS <= 1e-2 on bf16 outputs.
+Inputs come from the seeded generator; both sides see the same bf16 values.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.reference as R
+from trainable_block_sparse_compress_amd import binding as B
+from trainable_block_sparse_compress_amd import datagen as D
+from trainable_block_sparse_compress_amd import pipeline as P
+from tests.gpu_util import f64_to_bits, i32, say, to_bits, to_dev, to_f64
+from tests.helpers import (ATT_MAX_ABS, ATT_REL_RMS, attn_errors, check_selection,
+                           sample_positions)
+
+pytestmark = pytest.mark.gpu
+
+
+def _starts(lengths):
+    st = [0]
+    for n in lengths[:-1]:
+        st.append(st[-1] + n)
+    return st
+
+
+def _cfg(p: R.Params, **kw):
+    return P.SparseConfig(n_init=p.n_init, n_local=p.n_local, n_topk=p.n_topk,
+                          lse_mode=p.lse_mode, **kw)
+
+
+# ----------------------------------------------------------------------------
+# compress_k
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lengths,h_kv,kl", [
+    ([4096], 1, (32, 16)),
+    ([3000, 77, 31, 1000], 2, (32, 16)),
+    ([3000, 77, 130, 1000], 2, (128, 64)),
+    ([131072], 2, (32, 16)),
+])
+def test_compress_bit_exact(lib, lengths, h_kv, kl):
+    say(f"compress_k lengths={lengths} h_kv={h_kv} kernel/stride={kl}")
+    inp = D.make_prefill(21, lengths, h_q=h_kv, h_kv=h_kv)
+    k = to_dev(inp.k)
+    nw = [P.n_windows(n, *kl) for n in lengths]
+    offs = _starts(nw)
+    kc = torch.zeros((h_kv, max(1, sum(nw)), 128), dtype=torch.bfloat16, device="cuda")
+    B.compress_k(k, i32(_starts(lengths)), i32(lengths), len(lengths), max(lengths), kl[0], kl[1],
+                 i32(offs), kc)
+    torch.cuda.synchronize()
+    got = to_bits(kc)
+    st = _starts(lengths)
+    for s, n in enumerate(lengths):
+        ref = R.compress_keys(inp.k[st[s]:st[s] + n], kl[0], kl[1], round_bf16=True)
+        assert np.array_equal(got[:, offs[s]:offs[s] + nw[s]], f64_to_bits(ref)), f"sequence {s}"
+
+
+def test_compress_incremental(lib):
+    """Decode-style updates: windows completed by each new token are appended
+    in place and equal a full compression of the final cache."""
+    say("compress_k incremental")
+    cap, h_kv, lens0 = 1024, 2, [700, 129, 31]
+    inp = D.make_prefill(22, [cap] * 3, h_q=h_kv, h_kv=h_kv)
+    k = to_dev(inp.k)
+    cap1 = P.n_windows(cap, 32, 16)
+    kc = torch.zeros((h_kv, 3 * cap1, 128), dtype=torch.bfloat16, device="cuda")
+    cu_k, cu_c = i32([0, cap, 2 * cap]), i32([0, cap1, 2 * cap1])
+    lens = list(lens0)
+    B.compress_k(k, cu_k, i32(lens), 3, max(lens), 32, 16, cu_c, kc)
+    for _ in range(40):
+        begin = [P.n_windows(n, 32, 16) for n in lens]
+        lens = [n + 1 for n in lens]
+        B.compress_k(k, cu_k, i32(lens), 3, max(lens), 32, 16, cu_c, kc, cmp_begin=i32(begin),
+                     max_new=1)
+    torch.cuda.synchronize()
+    got = to_bits(kc)
+    for s, n in enumerate(lens):
+        ref = R.compress_keys(inp.k[s * cap:s * cap + n], 32, 16, round_bf16=True)
+        N = ref.shape[1]
+        assert np.array_equal(got[:, s * cap1:s * cap1 + N], f64_to_bits(ref))
+
+
+# ----------------------------------------------------------------------------
+# dense attention
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lengths,h_q,h_kv", [
+    ([1, 64, 65, 200, 1000], 32, 2),
+    ([777, 300], 2, 1),
+    ([513], 8, 1),
+])
+def test_dense_attention(lib, lengths, h_q, h_kv):
+    say(f"dense_attn lengths={lengths} h_q={h_q} h_kv={h_kv}")
+    inp = D.make_prefill(23, lengths, h_q, h_kv)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    st = _starts(lengths)
+    cfg = P.SparseConfig()
+    out = torch.empty_like(q)
+    lse = torch.empty((h_q, q.shape[0]), dtype=torch.float32, device="cuda")
+    P.DensePlan(st, lengths, st, lengths, h_kv, cfg).run(q, k, v, out, lse)
+    torch.cuda.synchronize()
+    of, lf = to_f64(out), lse.cpu().numpy()
+    G, scale = h_q // h_kv, 1 / math.sqrt(128)
+    worst = 0.0
+    for s, n in enumerate(lengths):
+        Qs, Ks, Vs = R.as_f64(inp.q[st[s]:st[s] + n]), R.as_f64(inp.k[st[s]:st[s] + n]), R.as_f64(inp.v[st[s]:st[s] + n])
+        ref = R.dense_prefill(Qs, Ks, Vs, G, scale)
+        o_ref = np.stack([ref[t][0] for t in range(n)])
+        l_ref = np.stack([ref[t][1] for t in range(n)])
+        ma, rr = attn_errors(of[st[s]:st[s] + n], o_ref)
+        worst = max(worst, ma)
+        assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (s, ma, rr)
+        assert np.abs(lf[:, st[s]:st[s] + n].T - l_ref).max() < 1e-3
+    say(f"  max abs err {worst:.3e}")
+
+
+# ----------------------------------------------------------------------------
+# sparse attention on given block lists (selection noise excluded)
+# ----------------------------------------------------------------------------
+
+def _random_lists(lengths, h_kv, p: R.Params, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = sum(lengths)
+    idx = np.full((h_kv, rows, p.n_sel), -1, dtype=np.int32)
+    lists = {}
+    st = _starts(lengths)
+    for s, n in enumerate(lengths):
+        for t in range(n):
+            bt = t // 64
+            for g in range(h_kv):
+                fixed = set(range(min(p.n_init, bt + 1))) | set(range(max(0, bt - p.n_local + 1), bt + 1))
+                rest = [b for b in range(bt + 1) if b not in fixed]
+                kk = min(len(rest), p.n_topk)
+                pick = set(rng.choice(rest, size=kk, replace=False).tolist()) if kk else set()
+                bl = sorted(fixed | pick)
+                idx[g, st[s] + t, :len(bl)] = bl
+                lists[(s, t, g)] = bl
+    return idx, lists
+
+
+@pytest.mark.parametrize("lengths,h_q,h_kv,sel", [
+    ([4096], 2, 1, (1, 4, 11)),
+    ([3000, 700], 32, 2, (1, 4, 11)),
+    ([2500], 32, 2, (0, 0, 9)),       # generic lists: the query's own block may or may not appear
+    ([1000, 37], 16, 2, (2, 3, 5)),
+])
+def test_sparse_attention_given_lists(lib, lengths, h_q, h_kv, sel):
+    say(f"sparse_attn lists lengths={lengths} h_q={h_q} h_kv={h_kv} sel={sel}")
+    p = R.Params(n_init=sel[0], n_local=sel[1], n_topk=sel[2])
+    inp = D.make_prefill(24, lengths, h_q, h_kv)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    idx_np, lists = _random_lists(lengths, h_kv, p, seed=5)
+    idx = torch.from_numpy(idx_np).cuda()
+    st = _starts(lengths)
+    out = torch.empty_like(q)
+    lse = torch.empty((h_q, q.shape[0]), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, B.attn_workspace(h_kv, len(lengths), max(lengths), max(lengths))),
+                     dtype=torch.uint8, device="cuda")
+    B.sparse_attn(q, k, v, i32(st), i32(lengths), i32(st), i32(lengths), len(lengths),
+                  max(lengths), max(lengths), idx, p.n_init, p.n_local, 1 / math.sqrt(128), out,
+                  lse, ws)
+    torch.cuda.synchronize()
+    of, lf = to_f64(out), lse.cpu().numpy()
+    G = h_q // h_kv
+    worst = 0.0
+    for s, n in enumerate(lengths):
+        Ks, Vs = R.as_f64(inp.k[st[s]:st[s] + n]), R.as_f64(inp.v[st[s]:st[s] + n])
+        pos = range(n) if n * h_q <= 8192 * 8 else sample_positions(n, 160, seed=s)
+        for t in pos:
+            o_ref, l_ref = R.attend_token(inp.q[st[s] + t], t, Ks, Vs,
+                                          [lists[(s, t, g)] for g in range(h_kv)], G, p)
+            ma, rr = attn_errors(of[st[s] + t], o_ref)
+            worst = max(worst, ma)
+            assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (s, t, ma, rr)
+            assert np.abs(lf[:, st[s] + t] - l_ref).max() < 1e-3, (s, t)
+    say(f"  max abs err {worst:.3e}")
+
+
+# ----------------------------------------------------------------------------
+# selection
+# ----------------------------------------------------------------------------
+
+def _run_select(inp, lengths, h_q, h_kv, p: R.Params):
+    st = _starts(lengths)
+    plan = P.SparsePlan(st, lengths, st, lengths, sum(lengths), h_q, h_kv, _cfg(p))
+    q, k = to_dev(inp.q), to_dev(inp.k)
+    plan.compress(k)
+    plan.select(q)
+    torch.cuda.synchronize()
+    lse = plan.ws_select[:h_q * sum(lengths) * 4].view(torch.float32).view(h_q, sum(lengths))
+    return plan, plan.block_idx.cpu().numpy(), lse.cpu().numpy()
+
+
+def _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, positions_by_seq):
+    pr = p.with_(round_kc=True)
+    st = _starts(lengths)
+    G = h_q // h_kv
+    stats = {"rows": 0, "scored": 0, "exempt": 0, "band": 0}
+    for s, n in enumerate(lengths):
+        Ks = inp.k[st[s]:st[s] + n]
+        KC1 = R.compress_keys(Ks, 32, 16, True)
+        KC2 = R.compress_keys(Ks, 128, 64, True) if p.lse_mode == "approx" else None
+        for t in positions_by_seq[s]:
+            sel, diag = R.select_token(inp.q[st[s] + t], t, KC1, KC2, G, pr)
+            if diag["scored"]:
+                stats["scored"] += 1
+                L_gpu = lse[:, st[s] + t]
+                assert np.abs(L_gpu - diag["L"]).max() < 1e-3, (s, t, "lse")
+            for g in range(h_kv):
+                gl = [int(b) for b in idx[g, st[s] + t] if b >= 0]
+                ok, exempt, band = check_selection(gl, sel[g], diag["info"][g], t, pr)
+                assert ok, (s, t, g, gl, sel[g])
+                stats["exempt"] += int(exempt)
+                stats["band"] += band
+                stats["rows"] += 1
+    return stats
+
+
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_select_tiny_all_rows(lib, mode):
+    """Tiny case, one KV head, G = 2, n = 4096, |I| = 1 + 4 + 11; every row."""
+    say(f"select tiny {mode}")
+    lengths, h_q, h_kv = [4096], 2, 1
+    p = R.Params(n_init=1, n_local=4, n_topk=11, lse_mode=mode)
+    inp = D.make_prefill(1, lengths, h_q, h_kv)
+    _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
+    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, [range(4096)])
+    say(f"  {stats}")
+
+
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_select_group16_ragged(lib, mode):
+    """32q/2kv, |I| = 96, two ragged sequences; sampled rows incl. every
+    boundary where rows start needing scores."""
+    say(f"select G=16 ragged {mode}")
+    lengths, h_q, h_kv = [9001, 6300], 32, 2
+    p = R.Params(lse_mode=mode)
+    inp = D.make_prefill(6, lengths, h_q, h_kv, n_needles=4)
+    _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
+    pos = [sample_positions(n, 40, seed=s, must=(6143, 6144, 6145, 6207, 6208)) for s, n in enumerate(lengths)]
+    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos)
+    say(f"  {stats}")
+
+
+# ----------------------------------------------------------------------------
+# end-to-end sparse path
+# ----------------------------------------------------------------------------
+
+def _e2e(inp, lengths, h_q, h_kv, p: R.Params, positions_by_seq, check_sel=True):
+    st = _starts(lengths)
+    plan = P.SparsePlan(st, lengths, st, lengths, sum(lengths), h_q, h_kv, _cfg(p))
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    out = torch.empty_like(q)
+    lse_o = torch.empty((h_q, q.shape[0]), dtype=torch.float32, device="cuda")
+    plan.run(q, k, v, out, lse_o)
+    torch.cuda.synchronize()
+    idx = plan.block_idx.cpu().numpy()
+    lse_s = plan.ws_select[:h_q * sum(lengths) * 4].view(torch.float32).view(h_q, sum(lengths)).cpu().numpy()
+    if check_sel:
+        stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse_s, positions_by_seq)
+        say(f"  selection {stats}")
+    of, lf = to_f64(out), lse_o.cpu().numpy()
+    G = h_q // h_kv
+    worst = 0.0
+    for s, n in enumerate(lengths):
+        Ks, Vs = R.as_f64(inp.k[st[s]:st[s] + n]), R.as_f64(inp.v[st[s]:st[s] + n])
+        for t in positions_by_seq[s]:
+            gl = [[int(b) for b in idx[g, st[s] + t] if b >= 0] for g in range(h_kv)]
+            o_ref, l_ref = R.attend_token(inp.q[st[s] + t], t, Ks, Vs, gl, G, p)
+            ma, rr = attn_errors(of[st[s] + t], o_ref)
+            worst = max(worst, ma)
+            assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (s, t, ma, rr)
+            assert np.abs(lf[:, st[s] + t] - l_ref).max() < 1e-3
+    say(f"  attention max abs err {worst:.3e}")
+    return plan, out
+
+
+def test_tiny_full_budget_equals_dense(lib):
+    """|I| = 64 covers all 64 blocks of n = 4096: the sparse path must equal
+    dense causal attention (oracle dense and the GPU dense kernel)."""
+    say("tiny |I|=64 == dense")
+    lengths, h_q, h_kv = [4096], 2, 1
+    p = R.Params(n_init=1, n_local=4, n_topk=59)
+    inp = D.make_prefill(1, lengths, h_q, h_kv)
+    plan, out = _e2e(inp, lengths, h_q, h_kv, p, [range(0, 4096, 7)], check_sel=False)
+    idx = plan.block_idx.cpu().numpy()
+    for t in range(4096):
+        assert list(idx[0, t][:t // 64 + 1]) == list(range(t // 64 + 1))
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    dense = torch.empty_like(q)
+    P.DensePlan([0], [4096], [0], [4096], h_kv, P.SparseConfig()).run(q, k, v, dense)
+    Qf, Kf, Vf = R.as_f64(inp.q), R.as_f64(inp.k), R.as_f64(inp.v)
+    ref = R.dense_prefill(Qf, Kf, Vf, 2, 1 / math.sqrt(128), positions=range(0, 4096, 5))
+    o_ref = np.stack([ref[t][0] for t in ref])
+    of = to_f64(out)[list(ref)]
+    ma, rr = attn_errors(of, o_ref)
+    assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS
+    assert (out.float() - dense.float()).abs().max().item() <= 2 * 2.0 ** -8
+
+
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_tiny_end_to_end(lib, mode):
+    say(f"tiny end-to-end {mode}")
+    p = R.Params(n_init=1, n_local=4, n_topk=11, lse_mode=mode)
+    inp = D.make_prefill(1, [4096], 2, 1)
+    _e2e(inp, [4096], 2, 1, p, [range(0, 4096, 3)])
+
+
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_32k_sampled(lib, mode):
+    """Single layer of the 8B shape at n = 32768 with 8 needle blocks."""
+    say(f"32K end-to-end {mode}")
+    n = 32768
+    p = R.Params(lse_mode=mode)
+    inp = D.make_prefill(2, n, 32, 2, n_needles=8)
+    pos = sample_positions(n, 24, seed=2, must=(6143, 6144, 20000 - 1))
+    _e2e(inp, [n], 32, 2, p, [pos])
+
+
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_128k_sampled(lib, mode):
+    """n = 131072 (2048 blocks) with 32 needle blocks; sampled rows."""
+    say(f"128K end-to-end {mode}")
+    n = 131072
+    p = R.Params(lse_mode=mode)
+    inp = D.make_prefill(3, n, 32, 2, n_needles=32)
+    pos = sample_positions(n, 10, seed=3, must=(6144, 131071))
+    _e2e(inp, [n], 32, 2, p, [pos])
+
+
+def test_varlen_switch(lib):
+    """Packed batch of 65536 tokens, lengths from the four buckets; <= 8192
+    takes the dense path, longer sequences the sparse path."""
+    lengths = D.varlen_lengths(5)
+    say(f"varlen switch lengths={lengths}")
+    h_q, h_kv = 32, 2
+    inp = D.make_prefill(5, lengths, h_q, h_kv)
+    cfg = P.SparseConfig()
+    plan = P.SwitchPlan(lengths, h_q, h_kv, cfg)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    out = torch.empty_like(q)
+    plan.run(q, k, v, out)
+    torch.cuda.synchronize()
+    of = to_f64(out)
+    idx = plan.sparse.block_idx.cpu().numpy()
+    st = _starts(lengths)
+    p = R.Params()
+    pr = p.with_(round_kc=True)
+    for s, n in enumerate(lengths):
+        Qs, Ks, Vs = inp.q[st[s]:st[s] + n], R.as_f64(inp.k[st[s]:st[s] + n]), R.as_f64(inp.v[st[s]:st[s] + n])
+        pos = sample_positions(n, 6, seed=s)
+        if n <= cfg.threshold:
+            ref = R.dense_prefill(Qs, Ks, Vs, 16, 1 / math.sqrt(128), positions=pos)
+            for t in pos:
+                ma, rr = attn_errors(of[st[s] + t], ref[t][0])
+                assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, ("dense", s, t, ma)
+        else:
+            KC1 = R.compress_keys(inp.k[st[s]:st[s] + n], 32, 16, True)
+            for t in pos:
+                sel, diag = R.select_token(Qs[t], t, KC1, None, 16, pr)
+                gl = [[int(b) for b in idx[g, st[s] + t] if b >= 0] for g in range(h_kv)]
+                for g in range(h_kv):
+                    ok, _, _ = check_selection(gl[g], sel[g], diag["info"][g], t, pr)
+                    assert ok, ("sparse select", s, t, g)
+                o_ref, _ = R.attend_token(Qs[t], t, Ks, Vs, gl, 16, p)
+                ma, rr = attn_errors(of[st[s] + t], o_ref)
+                assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, ("sparse", s, t, ma)
+
+
+def test_decode_steps(lib):
+    """Decode: incremental compression, selection for one new token per
+    sequence and sparse attention over a transposed V cache, checked at
+    every step against the oracle's row for that position."""
+    say("decode steps")
+    batch, h_q, h_kv, steps = 3, 32, 2, 6
+    lens0 = [7000, 9001, 6400]
+    cap = 9088
+    p = R.Params()
+    pr = p.with_(round_kc=True)
+    inp = D.make_prefill(4, [cap] * batch, h_q, h_kv, n_needles=4)
+    st = _starts([cap] * batch)
+    cfg = _cfg(p)
+    dec = P.DecodeState(batch, cap, h_q, h_kv, cfg)
+    kt, vt = to_dev(inp.k), to_dev(inp.v)
+    dec.fill([kt[st[s]:st[s] + lens0[s]] for s in range(batch)],
+             [vt[st[s]:st[s] + lens0[s]] for s in range(batch)], lens0)
+    qt = to_dev(inp.q)
+    out = torch.empty((batch, h_q, 128), dtype=torch.bfloat16, device="cuda")
+    for step in range(steps):
+        pos = [dec.lens[s] for s in range(batch)]          # position of the new token
+        k_new = torch.stack([kt[st[s] + pos[s]] for s in range(batch)])
+        v_new = torch.stack([vt[st[s] + pos[s]] for s in range(batch)])
+        q_new = torch.stack([qt[st[s] + pos[s]] for s in range(batch)]).contiguous()
+        old = dec.append(k_new, v_new)
+        dec.step_prepare(old)
+        dec.step(q_new, out, max(dec.lens))
+        torch.cuda.synchronize()
+        idx = dec.block_idx.cpu().numpy()
+        of = to_f64(out)
+        for s in range(batch):
+            t = pos[s]
+            Ks = inp.k[st[s]:st[s] + t + 1]
+            KC1 = R.compress_keys(Ks, 32, 16, True)
+            sel, diag = R.select_token(inp.q[st[s] + t], t, KC1, None, 16, pr)
+            gl = [[int(b) for b in idx[g, s] if b >= 0] for g in range(h_kv)]
+            for g in range(h_kv):
+                ok, _, _ = check_selection(gl[g], sel[g], diag["info"][g], t, pr)
+                assert ok, (step, s, g)
+            o_ref, _ = R.attend_token(inp.q[st[s] + t], t, R.as_f64(Ks), R.as_f64(inp.v[st[s]:st[s] + t + 1]), gl, 16, p)
+            ma, rr = attn_errors(of[s], o_ref)
+            assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (step, s, ma, rr)
+
+
+def test_deterministic(lib):
+    say("determinism")
+    n = 8192
+    inp = D.make_prefill(9, n, 32, 2, n_needles=4)
+    plan = P.SparsePlan([0], [n], [0], [n], n, 32, 2, P.SparseConfig())
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    outs, idxs = [], []
+    for _ in range(2):
+        out = torch.empty_like(q)
+        plan.run(q, k, v, out)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+        idxs.append(plan.block_idx.clone())
+    assert torch.equal(idxs[0], idxs[1])
+    assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))

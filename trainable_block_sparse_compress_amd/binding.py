@@ -1,0 +1,182 @@
+"""Thin ctypes binding of ``libinfllmv2.so`` (the C ABI in include/infllmv2.h).
+
+Argument marshalling only: every function takes torch tensors that already
+live on the GPU, passes their device pointers and shapes to the entry point of
+the same name, and raises ``InfLLMv2Error`` on a non-zero return code.  Every
+step of the computation runs in the library's HIP kernels; there is no
+fallback.  PyTorch provides device memory and the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "InfLLMv2Error", "load", "library_path", "version", "compress_k", "select_blocks",
+    "select_blocks_workspace", "sparse_attn", "dense_attn", "attn_workspace",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "lib", "libinfllmv2.so")
+_lib = None
+
+_P = ctypes.c_void_p
+_I32 = ctypes.c_int32
+_I64 = ctypes.c_int64
+_F = ctypes.c_float
+_SZP = ctypes.POINTER(ctypes.c_size_t)
+
+_SIGS = {
+    "infllmv2_compress_k": [_P, _P, _P, _I32, _I32, _I64, _I32, _I32, _I32, _I32, _P, _P, _I32,
+                            _I64, _P, _P],
+    "infllmv2_select_blocks": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64,
+                               _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                               _I32, _I32, _I32, _I32, _F, _P, _SZP, _P, _P],
+    "infllmv2_sparse_attn": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32, _I32,
+                             _I32, _I32, _P, _I32, _I32, _I32, _F, _I64, _P, _P, _P, _SZP, _P],
+    "infllmv2_dense_attn": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32, _I32,
+                            _I32, _F, _I64, _P, _P, _P, _SZP, _P],
+}
+
+
+class InfLLMv2Error(RuntimeError):
+    pass
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load the library (once).  Fails loudly when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise InfLLMv2Error(f"{_LIB_PATH} is missing: build it first (python "
+                                "trainable_block_sparse_compress_amd/build.py)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, args in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = ctypes.c_int
+        for name in ("infllmv2_strerror",):
+            getattr(lib, name).argtypes = [ctypes.c_int]
+            getattr(lib, name).restype = ctypes.c_char_p
+        for name in ("infllmv2_last_error", "infllmv2_version"):
+            getattr(lib, name).argtypes = []
+            getattr(lib, name).restype = ctypes.c_char_p
+        _lib = lib
+    return _lib
+
+
+def version() -> str:
+    return load().infllmv2_version().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        lib = load()
+        raise InfLLMv2Error(f"{lib.infllmv2_strerror(rc).decode()} ({rc}): "
+                            f"{lib.infllmv2_last_error().decode()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise InfLLMv2Error("tensors passed to the library must be on the GPU")
+    if not t.is_contiguous():
+        raise InfLLMv2Error("tensors passed to the library must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t, name):
+    if t is not None and t.dtype != torch.int32:
+        raise InfLLMv2Error(f"{name} must be int32")
+    return _ptr(t)
+
+
+def _bf16(t, name):
+    if t is not None and t.dtype != torch.bfloat16:
+        raise InfLLMv2Error(f"{name} must be bfloat16")
+    return _ptr(t)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def compress_k(k, cu_seqlens_k, seqused_k, batch, max_seqlen_k, kernel_size, stride, cu_cmp,
+               k_cmp, cmp_begin=None, max_new=0):
+    """k [rows_k, h_kv, d] bf16 -> k_cmp [h_kv, c_rows, d] bf16 (in place)."""
+    rows_k, h_kv, d = k.shape
+    _check(load().infllmv2_compress_k(
+        _bf16(k, "k"), _i32(cu_seqlens_k, "cu_seqlens_k"), _i32(seqused_k, "seqused_k"), batch,
+        max_seqlen_k, rows_k, h_kv, d, kernel_size, stride, _i32(cu_cmp, "cu_cmp"),
+        _i32(cmp_begin, "cmp_begin"), max_new, k_cmp.shape[1], _bf16(k_cmp, "k_cmp"), _stream()))
+
+
+def select_blocks_workspace(rows_q, h_q, h_kv, max_seqlen_q, max_seqlen_k, n_init, n_local,
+                            n_topk, approx=False) -> int:
+    size = ctypes.c_size_t(0)
+    _check(load().infllmv2_select_blocks(
+        None, None, _P(1) if approx else None, None, None, None, None, None, None, 1,
+        max_seqlen_q, max_seqlen_k, rows_q, 0, 0, h_q, h_kv, 128, 64, n_init, n_local, n_topk,
+        32, 16, 128, 64, 5, 4, 1, 1.0, None, ctypes.byref(size), None, None))
+    return size.value
+
+
+def select_blocks(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, cu_c1, cu_c2,
+                  batch, max_seqlen_q, max_seqlen_k, n_init, n_local, n_topk, softmax_scale,
+                  block_idx, workspace, block_size=64, c1=(32, 16), c2=(128, 64), pool=(5, 4, 1)):
+    """Writes block_idx [h_kv, rows_q, n_init + n_local + n_topk] int32."""
+    rows_q, h_q, d = q.shape
+    h_kv, c1_rows, _ = k_c1.shape
+    c2_rows = k_c2.shape[1] if k_c2 is not None else 0
+    size = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    _check(load().infllmv2_select_blocks(
+        _bf16(q, "q"), _bf16(k_c1, "k_c1"), _bf16(k_c2, "k_c2"), _i32(cu_seqlens_q, "cu_seqlens_q"),
+        _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
+        _i32(seqused_k, "seqused_k"), _i32(cu_c1, "cu_c1"), _i32(cu_c2, "cu_c2"), batch,
+        max_seqlen_q, max_seqlen_k, rows_q, c1_rows, c2_rows, h_q, h_kv, d, block_size, n_init,
+        n_local, n_topk, c1[0], c1[1], c2[0], c2[1], pool[0], pool[1], pool[2], softmax_scale,
+        _ptr(workspace), ctypes.byref(size), _i32(block_idx, "block_idx"), _stream()))
+
+
+def attn_workspace(h_kv, batch, max_seqlen_q, max_seqlen_k, v_seq_stride=0) -> int:
+    size = ctypes.c_size_t(0)
+    _check(load().infllmv2_dense_attn(
+        None, None, None, None, None, None, None, batch, max_seqlen_q, max_seqlen_k, 0, 0,
+        h_kv, h_kv, 128, 1.0, v_seq_stride, None, None, None, ctypes.byref(size), None))
+    return size.value
+
+
+def sparse_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch, max_seqlen_q,
+                max_seqlen_k, block_idx, n_init, n_local, softmax_scale, out, lse=None,
+                workspace=None, v_seq_stride=0, block_size=64):
+    rows_q, h_q, d = q.shape
+    rows_k, h_kv, _ = k.shape
+    n_sel = block_idx.shape[-1]
+    size = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
+    _check(load().infllmv2_sparse_attn(
+        _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _i32(cu_seqlens_q, "cu_seqlens_q"),
+        _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
+        _i32(seqused_k, "seqused_k"), batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, h_q,
+        h_kv, d, block_size, _i32(block_idx, "block_idx"), n_sel, n_init, n_local, softmax_scale,
+        v_seq_stride, _bf16(out, "out"), _ptr(lse), _ptr(workspace), ctypes.byref(size),
+        _stream()))
+
+
+def dense_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch, max_seqlen_q,
+               max_seqlen_k, softmax_scale, out, lse=None, workspace=None, v_seq_stride=0):
+    rows_q, h_q, d = q.shape
+    rows_k, h_kv, _ = k.shape
+    size = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
+    _check(load().infllmv2_dense_attn(
+        _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _i32(cu_seqlens_q, "cu_seqlens_q"),
+        _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
+        _i32(seqused_k, "seqused_k"), batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, h_q,
+        h_kv, d, softmax_scale, v_seq_stride, _bf16(out, "out"), _ptr(lse), _ptr(workspace),
+        ctypes.byref(size), _stream()))

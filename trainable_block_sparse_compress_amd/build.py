@@ -1,0 +1,65 @@
+"""Build the gfx950 HIP library ``lib/libinfllmv2.so`` in-tree with hipcc.
+
+Each ``csrc/*.hip`` file is compiled to an object under ``_build/`` (in
+parallel), then linked into one shared library.  The host pass of hipcc warns
+that it does not know the ``packed-fp32-ops`` feature; that is expected (the
+flag only concerns the device pass, where packed FP32 instructions are
+switched off).
+"""
+from __future__ import annotations
+
+import concurrent.futures
+import glob
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD = os.path.join(HERE, "_build")
+LIBDIR = os.path.join(HERE, "lib")
+LIB = os.path.join(LIBDIR, "libinfllmv2.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+ARCH = "gfx950"
+CFLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{os.path.join(ROOT, 'include')}", f"-I{CSRC}",
+    "-Wall", "-Wno-unused-function",
+]
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
+    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
+                    if "packed-fp32-ops" not in line)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{out}")
+    if out.strip():
+        sys.stderr.write(out + "\n")
+    return obj
+
+
+def build(jobs: int | None = None) -> str:
+    """Compile every HIP source and link the library; returns its path."""
+    os.makedirs(BUILD, exist_ok=True)
+    os.makedirs(LIBDIR, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = jobs or min(8, len(srcs))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build())

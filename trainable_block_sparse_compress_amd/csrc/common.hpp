@@ -1,0 +1,97 @@
+// Device-side building blocks shared by the gfx950 kernels of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace infllmv2 {
+
+constexpr int kHeadDim = 128;
+constexpr int kBlock = 64;   // tokens per attention block
+constexpr int kWave = 64;    // CDNA wavefront
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float floatx4 __attribute__((__vector_size__(4 * sizeof(float))));
+typedef unsigned int u32x4 __attribute__((__vector_size__(4 * sizeof(unsigned int))));
+
+// ---------------------------------------------------------------------------
+// MFMA: D(16x16 f32) += A(16x32 bf16) * B(32x16 bf16).
+// Lane l holds A row (l % 16), B column (l % 16), reduction slots 8*(l/16)+v;
+// D column (l % 16), rows 4*(l/16)+v.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ u32x4 as_u32x4(bf16x8 v) { return __builtin_bit_cast(u32x4, v); }
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+__device__ __forceinline__ void stg16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+__device__ __forceinline__ u32x4 zero16() { return u32x4{0u, 0u, 0u, 0u}; }
+
+// float -> bf16 bits, round to nearest even (NaN not expected on this path).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Cross-lane reductions between the two 32-lane halves and between odd and
+// even 16-lane rows (gfx950 v_permlane32_swap / v_permlane16_swap).  Swapping
+// a register with itself leaves each lane with its own value in one result
+// and its partner's in the other, so the symmetric combination of the two
+// results is the pairwise reduction in every lane.
+__device__ __forceinline__ float sum_x32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_x16(float v) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+// Reduce-scatter of two registers across the 32-lane halves: one half ends
+// with a's half-sum, the other with b's.
+__device__ __forceinline__ float rs_x32(float a, float b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+// Same across odd/even 16-lane rows.
+__device__ __forceinline__ float rs_x16(float a, float b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sequence description shared by the kernels: start row and length.
+struct SeqRange {
+  int start;
+  int len;
+};
+__device__ __forceinline__ SeqRange seq_range(const int32_t* cu, const int32_t* used, int s) {
+  SeqRange r;
+  r.start = cu[s];
+  r.len = used ? used[s] : (cu[s + 1] - cu[s]);
+  if (r.start < 0 || r.len < 0) {
+    r.start = 0;
+    r.len = 0;
+  }
+  return r;
+}
+
+}  // namespace infllmv2

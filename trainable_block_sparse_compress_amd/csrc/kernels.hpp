@@ -1,0 +1,89 @@
+// Kernel argument blocks and launchers of the gfx950 library.
+#pragma once
+
+#include "common.hpp"
+
+namespace infllmv2 {
+
+struct CompressArgs {
+  const uint16_t* k;        // [rows_k, h_kv, 128]
+  const int32_t* cu_k;
+  const int32_t* used_k;
+  int64_t rows_k;
+  int h_kv;
+  int kernel, stride;
+  const int32_t* cu_cmp;
+  const int32_t* cmp_begin;
+  int max_new;
+  int64_t c_rows;
+  uint16_t* k_cmp;          // [h_kv, c_rows, 128]
+};
+
+struct TransposeArgs {
+  const uint16_t* v;        // [rows_k, h_kv, 128]
+  const int32_t* cu_k;
+  const int32_t* used_k;
+  int64_t rows_k;
+  int h_kv, batch;
+  int64_t ld;               // padded keys per sequence (multiple of 64)
+  uint16_t* vt;             // [h_kv, 128, batch, ld]
+};
+
+struct ScoreArgs {
+  const uint16_t* q;        // [rows_q, h_q, 128]
+  const uint16_t* kc;       // [h_kv, c_rows, 128] compressed keys
+  const int32_t* cu_q;
+  const int32_t* used_q;
+  const int32_t* cu_k;
+  const int32_t* used_k;
+  const int32_t* cu_c;      // first compressed row per sequence
+  int64_t rows_q, c_rows;
+  int h_q, h_kv, G;
+  int win_kernel, win_stride;
+  int n_init, n_local, n_topk;
+  float scale;              // softmax scale
+  float c;                  // scale * log2(e)
+  float* lse;               // [h_q, rows_q], natural log
+  float* bs;                // [h_kv, rows_q, bs_ld] block scores
+  int64_t bs_ld;
+};
+
+struct TopkArgs {
+  const float* bs;          // [h_kv, rows_q, bs_ld]
+  int64_t bs_ld;
+  const int32_t* cu_q;
+  const int32_t* used_q;
+  const int32_t* cu_k;
+  const int32_t* used_k;
+  int64_t rows_q;
+  int n_init, n_local, n_topk;
+  int32_t* idx;             // [h_kv, rows_q, n_sel]
+};
+
+struct AttnArgs {
+  const uint16_t* q;        // [rows_q, h_q, 128]
+  const uint16_t* k;        // [rows_k, h_kv, 128]
+  const uint16_t* vt;       // [h_kv, 128, batch, vt_ld]
+  const int32_t* cu_q;
+  const int32_t* used_q;
+  const int32_t* cu_k;
+  const int32_t* used_k;
+  int64_t rows_q, rows_k, vt_ld;
+  int batch, h_q, h_kv, G;
+  const int32_t* bidx;      // [h_kv, rows_q, n_sel] or nullptr (dense)
+  int n_sel, n_init, n_local;
+  float scale, c;
+  uint16_t* out;            // [rows_q, h_q, 128]
+  float* lse;               // [h_q, rows_q] or nullptr
+};
+
+// Launchers (return the launch status; no synchronisation).
+hipError_t launch_compress(const CompressArgs& a, int batch, int max_windows, hipStream_t st);
+hipError_t launch_transpose_v(const TransposeArgs& a, hipStream_t st);
+hipError_t launch_score_lse(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st);
+hipError_t launch_score_blocks(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st);
+hipError_t launch_topk(const TopkArgs& a, int batch, int h_kv, int max_seqlen_q, int max_blocks,
+                       hipStream_t st);
+hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st);
+
+}  // namespace infllmv2

@@ -1,0 +1,263 @@
+// Block scoring on bf16 MFMA: stages 2 and 3 of the three-stage block
+// representation (top168.com article on InfLLM-V2, section 三 "块表示的三阶段压缩")
+// with the hardware-aware two-pass scheme of section 四 "高效实现的技术突破".
+//
+//   pass 1 (score_lse_kernel):    L[t, h] = log sum_j exp(scale * q[t,h] . kc[g, j])
+//                                  over the windows j visible to t.  Run on the
+//                                  stage-1 keys it is exact; run on the coarse
+//                                  keys (kernel 128, stride 64) it is the LSE
+//                                  approximation.
+//   pass 2 (score_blocks_kernel): p[t, h, j] = exp(scale * q[t,h] . kc1[g, j] - L[t, h]),
+//                                  S[t, g, j] = sum over the group's heads of p,
+//                                  score[t, g, b] = max_{j = 4b-1 .. 4b+3} S[t, g, j].
+//                                  The group sum and the max pool happen in
+//                                  registers; only block scores reach HBM.
+//
+// Tiling: a workgroup owns 16 query tokens of one sequence and one KV group
+// (4 waves x 4 tokens).  For one token the 16 heads of its group are the 16
+// rows of a 16x16x32 MFMA tile and 16 compressed keys its columns, so each
+// lane ends up holding 4 heads of one window: the group sum is 3 in-lane adds
+// plus a reduce-scatter over the four 16-lane rows, after which lane l holds
+// S for window (tile start + l) and a quad max gives the block score.
+// Compressed-key tiles of 64 windows are staged in LDS and shared by the 4
+// waves; each LDS fragment feeds 4 MFMAs (one per token).  Group sizes below
+// 16 pad the head rows with zeros.
+#include "kernels.hpp"
+
+namespace infllmv2 {
+
+namespace {
+
+constexpr int kQT = 16;      // query tokens per workgroup
+constexpr int kTPW = 4;      // tokens per wave
+constexpr int kWT = 64;      // windows per tile
+
+__device__ __forceinline__ int n_visible(int t, int win_kernel, int win_stride, int nwin) {
+  if (t < win_kernel - 1) return 0;
+  return min(nwin, (t - win_kernel + 1) / win_stride + 1);
+}
+
+// Stage kc[g, cu_c + j0 .. j0+63] into LDS: 64 rows of 256 bytes, 16-byte
+// chunks XOR-swizzled by the row so that 8 consecutive rows read at the same
+// chunk hit distinct banks.
+__device__ __forceinline__ void stage_windows(uint8_t* lds, const ScoreArgs& a, int g, int64_t c0,
+                                              int j0, int nwin) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int w = (tid >> 4) + 16 * it;
+    const int ch = tid & 15;
+    const int j = j0 + w;
+    const int64_t row = c0 + j;
+    u32x4 v = zero16();
+    if (j < nwin && row >= 0 && row < a.c_rows) v = ldg16(a.kc + ((int64_t)g * a.c_rows + row) * kHeadDim + 8 * ch);
+    *reinterpret_cast<u32x4*>(lds + w * 256 + ((ch ^ (w & 7)) << 4)) = v;
+  }
+}
+
+__device__ __forceinline__ bf16x8 lds_window_frag(const uint8_t* lds, int w, int ch) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + w * 256 + ((ch ^ (w & 7)) << 4)));
+}
+
+template <int PASS>
+__device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
+  const int s = blockIdx.z;
+  const int g = blockIdx.y;
+  const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
+  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
+  const int i0 = blockIdx.x * kQT;
+  if (i0 >= rq.len) return;
+  const int pos0 = rk.len - rq.len;
+  const int nq = min(kQT, rq.len - i0);
+  const int t_first = pos0 + i0;
+  const int t_last = t_first + nq - 1;
+  const int n_sel = a.n_init + a.n_local + a.n_topk;
+  // Rows whose candidate count does not exceed n_topk keep every block; none
+  // of them needs scores.
+  if (t_last < n_sel * kBlock) return;
+  const int nwin = rk.len >= a.win_kernel ? (rk.len - a.win_kernel) / a.win_stride + 1 : 0;
+
+  int j_begin, j_end;
+  if (PASS == 1) {
+    j_begin = 0;
+    j_end = n_visible(t_last, a.win_kernel, a.win_stride, nwin);
+  } else {
+    const int b_hi = t_last / kBlock - a.n_local;      // last candidate block in the tile
+    j_begin = max(0, 4 * a.n_init - 1) & ~(kWT - 1);
+    j_end = 4 * b_hi + 4;
+  }
+  if (j_end <= j_begin) return;
+
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int q4 = lane >> 4;
+  const int c16 = lane & 15;
+  const int64_t c0 = a.cu_c[s];
+
+  int tpos[kTPW], nv[kTPW], bt[kTPW];
+  int64_t trow[kTPW];
+  bool tval[kTPW], need[kTPW];
+  bf16x8 qa[kTPW][4];
+  float Lc[kTPW][4];
+#pragma unroll
+  for (int k = 0; k < kTPW; ++k) {
+    const int i = i0 + wave * kTPW + k;
+    tval[k] = i < rq.len;
+    tpos[k] = pos0 + i;
+    trow[k] = (int64_t)rq.start + i;
+    bt[k] = tpos[k] / kBlock;
+    need[k] = tval[k] && (bt[k] - a.n_local - a.n_init + 1 > a.n_topk) && trow[k] < a.rows_q;
+    nv[k] = n_visible(tpos[k], a.win_kernel, a.win_stride, nwin);
+    const bool hv = tval[k] && c16 < a.G && trow[k] < a.rows_q;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = zero16();
+      if (hv) v = ldg16(a.q + (trow[k] * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
+      qa[k][ks] = as_bf16x8(v);
+    }
+    if (PASS == 2) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int head = 4 * q4 + r;
+        float L = __builtin_inff();
+        if (need[k] && head < a.G) {
+          const float l = a.lse[(int64_t)(g * a.G + head) * a.rows_q + trow[k]];
+          if (l > -__builtin_inff()) L = l * 1.4426950408889634f;
+        }
+        Lc[k][r] = L;
+      }
+    }
+  }
+
+  float m[kTPW][4], ssum[kTPW][4], carry[kTPW];
+#pragma unroll
+  for (int k = 0; k < kTPW; ++k) {
+    carry[k] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      m[k][r] = -1e30f;
+      ssum[k][r] = 0.f;
+    }
+  }
+  const int nv_first = n_visible(t_first, a.win_kernel, a.win_stride, nwin);
+
+  for (int jt = j_begin; jt < j_end; jt += kWT) {
+    __syncthreads();
+    stage_windows(lds, a, g, c0, jt, nwin);
+    __syncthreads();
+
+    floatx4 acc[kTPW][4];
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k)
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 b = lds_window_frag(lds, 16 * ct + c16, 4 * ks + q4);
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k) acc[k][ct] = mfma16(qa[k][ks], b, acc[k][ct]);
+      }
+    }
+
+    const bool full = jt + kWT <= nv_first;  // every window of the tile visible to every token
+    if (PASS == 1) {
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float v[4];
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) {
+            const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+            v[ct] = ok ? acc[k][ct][r] : -__builtin_inff();
+          }
+          const float mt = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
+          const float mn = fmaxf(m[k][r], mt);
+          const float mc = mn * a.c;
+          float sacc = ssum[k][r] * fast_exp2((m[k][r] - mn) * a.c);
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) sacc += fast_exp2(fmaf(v[ct], a.c, -mc));
+          ssum[k][r] = sacc;
+          m[k][r] = mn;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k) {
+        float sct[4];
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+          float sum = 0.f;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) sum += fast_exp2(fmaf(acc[k][ct][r], a.c, -Lc[k][r]));
+          sct[ct] = ok ? sum : 0.f;
+        }
+        // Reduce-scatter over the four 16-lane rows: afterwards lane l holds
+        // the group sum for window jt + l.
+        const float S = rs_x16(rs_x32(sct[0], sct[2]), rs_x32(sct[1], sct[3]));
+        const float q1 = fmaxf(S, __shfl_xor(S, 1));
+        const float qm = fmaxf(q1, __shfl_xor(q1, 2));     // windows 4b .. 4b+3
+        float prev = __shfl_up(S, 1);                        // window 4b-1
+        if (lane == 0) prev = carry[k];
+        carry[k] = __shfl(S, 63);
+        if (need[k] && (lane & 3) == 0) {
+          const int b = (jt >> 2) + (lane >> 2);
+          if (b >= a.n_init && b <= bt[k] - a.n_local && b < a.bs_ld)
+            a.bs[((int64_t)g * a.rows_q + trow[k]) * a.bs_ld + b] = fmaxf(qm, prev);
+        }
+      }
+    }
+  }
+
+  if (PASS == 1) {
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float mm = m[k][r], ss = ssum[k][r];
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+          const float m2 = __shfl_xor(mm, off);
+          const float s2 = __shfl_xor(ss, off);
+          const float mn = fmaxf(mm, m2);
+          ss = ss * fast_exp2((mm - mn) * a.c) + s2 * fast_exp2((m2 - mn) * a.c);
+          mm = mn;
+        }
+        const int head = 4 * q4 + r;
+        if (c16 == 0 && tval[k] && head < a.G && trow[k] < a.rows_q) {
+          const float L = ss > 0.f ? mm * a.scale + logf(ss) : -__builtin_inff();
+          a.lse[(int64_t)(g * a.G + head) * a.rows_q + trow[k]] = L;
+        }
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void score_lse_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWT * 256];
+  score_body<1>(a, lds);
+}
+
+__global__ __launch_bounds__(256) void score_blocks_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWT * 256];
+  score_body<2>(a, lds);
+}
+
+}  // namespace
+
+hipError_t launch_score_lse(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st) {
+  dim3 grid((max_seqlen_q + kQT - 1) / kQT, a.h_kv, batch);
+  hipLaunchKernelGGL(score_lse_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_blocks(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st) {
+  dim3 grid((max_seqlen_q + kQT - 1) / kQT, a.h_kv, batch);
+  hipLaunchKernelGGL(score_blocks_kernel, grid, dim3(256), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace infllmv2

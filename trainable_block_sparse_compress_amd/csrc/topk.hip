@@ -1,0 +1,173 @@
+// Block selection: init ∪ local ∪ top-k (top168.com article on InfLLM-V2,
+// section 七 "技术实现的创新细节": a query in block b_i always attends the fixed
+// init blocks and its local blocks; top-k runs over the remaining blocks and
+// the attended set is the union).
+//
+// One wavefront per (query row, KV group).  Candidate scores (non-negative
+// floats) are held in registers as order-preserving integer keys (bits + 1,
+// 0 marks an empty slot).  A radix select over 8-bit digits with a 256-bin
+// LDS histogram finds the exact n_topk-th largest key T; the selected
+// candidates are every key > T plus the lowest-index keys == T needed to
+// reach n_topk (ties broken toward the lower block index).  Ballot prefix
+// counts then emit the blocks in ascending order: init blocks, selected
+// candidates, local blocks — already sorted because those ranges are
+// disjoint and ordered.
+#include "kernels.hpp"
+
+namespace infllmv2 {
+
+namespace {
+
+constexpr int kWavesPerWG = 4;
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) { return (1ull << lane) - 1ull; }
+
+template <int PER>
+__global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
+  __shared__ uint32_t hist_all[kWavesPerWG][256];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  uint32_t* hist = hist_all[wave];
+  const int s = blockIdx.z;
+  const int g = blockIdx.y;
+  const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
+  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
+  const int i = blockIdx.x * kWavesPerWG + wave;
+  if (i >= rq.len) return;
+  const int64_t row = (int64_t)rq.start + i;
+  if (row >= a.rows_q) return;
+  const int t = rk.len - rq.len + i;
+  const int bt = t / kBlock;
+  const int n_sel = a.n_init + a.n_local + a.n_topk;
+  int32_t* out = a.idx + ((int64_t)g * a.rows_q + row) * n_sel;
+  const int lo = a.n_init;
+  const int hi = (int)min((int64_t)(bt - a.n_local), a.bs_ld - 1);
+  const int nc = hi - lo + 1;
+
+  if (nc <= a.n_topk) {
+    // Every causal block is attended.
+    for (int e = lane; e < n_sel; e += 64) out[e] = e <= bt ? e : -1;
+    return;
+  }
+
+  const float* row_bs = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld + lo;
+  uint32_t key[PER];
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int c = lane + 64 * p;
+    key[p] = 0;
+    if (c < nc) {
+      key[p] = __float_as_uint(row_bs[c]) + 1u;
+      kmax = max(kmax, key[p]);
+      kmin = min(kmin, key[p]);
+    }
+  }
+  // Wave-wide extremes: bits above the highest differing bit are common to
+  // all keys, so the first digit starts right below them.
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+  }
+  const uint32_t diff = kmax ^ kmin;
+  const int top_bit = diff ? 31 - __clz((int)diff) : 0;
+  uint32_t prefix = diff ? (kmax & ~((top_bit >= 31) ? 0xFFFFFFFFu : ((2u << top_bit) - 1u))) : kmax;
+  uint32_t pmask = diff ? ~((top_bit >= 31) ? 0xFFFFFFFFu : ((2u << top_bit) - 1u)) : 0xFFFFFFFFu;
+  int kk = a.n_topk;
+
+  if (diff) {
+    for (int hb = top_bit; hb >= 0; hb -= 8) {
+      const int lob = max(0, hb - 7);
+      const int width = hb - lob + 1;
+      const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) hist[lane * 4 + b] = 0;
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+#pragma unroll
+      for (int p = 0; p < PER; ++p) {
+        if (key[p] != 0 && (key[p] & pmask) == prefix) atomicAdd(&hist[(key[p] >> lob) & dmask], 1u);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+      __builtin_amdgcn_wave_barrier();
+      // Lane l owns bins 4l .. 4l+3; count of keys in higher bins via a
+      // suffix scan over lanes.
+      uint32_t h4[4];
+      uint32_t local = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        h4[b] = hist[lane * 4 + b];
+        local += h4[b];
+      }
+      uint32_t suffix = local;  // inclusive: lanes >= lane
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_down((int)suffix, off);
+        if (lane + off < 64) suffix += o;
+      }
+      uint32_t cum = suffix - local;  // keys in bins above 4l+3
+      int found = -1, newk = 0;
+#pragma unroll
+      for (int b = 3; b >= 0; --b) {
+        if (found < 0 && cum < (uint32_t)kk && (uint32_t)kk <= cum + h4[b]) {
+          found = lane * 4 + b;
+          newk = kk - (int)cum;
+        }
+        cum += h4[b];
+      }
+      const uint64_t ball = __ballot(found >= 0);
+      const int src = __ffsll((unsigned long long)ball) - 1;
+      const int digit = __shfl(found, src);
+      kk = __shfl(newk, src);
+      prefix |= ((uint32_t)digit & dmask) << lob;
+      pmask |= dmask << lob;
+      __builtin_amdgcn_wave_barrier();
+    }
+  }
+  const uint32_t T = prefix;  // exact key of the n_topk-th largest
+
+  // Emit: init blocks, selected candidates ascending, local blocks.
+  const int n_init_eff = min(a.n_init, bt + 1);
+  for (int e = lane; e < n_init_eff; e += 64) out[e] = e;
+  int base = n_init_eff;
+  int eq_seen = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const bool gt = key[p] > T;
+    const bool eq = key[p] == T && key[p] != 0;
+    const uint64_t eqb = __ballot(eq);
+    const int eq_rank = eq_seen + __popcll(eqb & lanemask_lt(lane));
+    const bool take = gt || (eq && eq_rank < kk);
+    const uint64_t tb = __ballot(take);
+    const int pos = base + __popcll(tb & lanemask_lt(lane));
+    if (take && pos < n_init_eff + a.n_topk) out[pos] = lo + lane + 64 * p;
+    base += __popcll(tb);
+    eq_seen += __popcll(eqb);
+  }
+  base = n_init_eff + a.n_topk;
+  for (int r = lane; r < a.n_local; r += 64) out[base + r] = bt - a.n_local + 1 + r;
+}
+
+}  // namespace
+
+hipError_t launch_topk(const TopkArgs& a, int batch, int h_kv, int max_seqlen_q, int max_blocks,
+                       hipStream_t st) {
+  dim3 grid((max_seqlen_q + kWavesPerWG - 1) / kWavesPerWG, h_kv, batch);
+  const int need = (max_blocks + 63) / 64;
+  if (need <= 8) {
+    hipLaunchKernelGGL(topk_kernel<8>, grid, dim3(256), 0, st, a);
+  } else if (need <= 16) {
+    hipLaunchKernelGGL(topk_kernel<16>, grid, dim3(256), 0, st, a);
+  } else if (need <= 32) {
+    hipLaunchKernelGGL(topk_kernel<32>, grid, dim3(256), 0, st, a);
+  } else if (need <= 64) {
+    hipLaunchKernelGGL(topk_kernel<64>, grid, dim3(256), 0, st, a);
+  } else if (need <= 128) {
+    hipLaunchKernelGGL(topk_kernel<128>, grid, dim3(256), 0, st, a);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace infllmv2
