@@ -149,3 +149,12 @@ def test_switch_partition_and_window_counts():
         assert P.n_windows(n, *cfg.c1) == R.n_windows(n, 32, 16)
         assert P.n_windows(n, *cfg.c2) == R.n_windows(n, 128, 64)
     assert cfg.n_sel == 96
+
+
+def test_no_workspace_is_not_a_size_query(lib):
+    """A NULL workspace with a NULL size pointer must take the launch path
+    (here: rejected for NULL tensors), never the size-query path."""
+    rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 64, 64, 64, 64,
+                                 32, 2, 128, 0.088, 64, None, None, None, None, None)
+    assert rc == EINVAL
+    assert B._ws(None) == (None, None)

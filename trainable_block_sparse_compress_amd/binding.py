@@ -108,6 +108,14 @@ def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
+def _ws(workspace):
+    """(pointer, size pointer) for a caller workspace.  Without one, both are
+    NULL: a NULL workspace with a non-NULL size pointer would be a size query."""
+    if workspace is None:
+        return None, None
+    return _ptr(workspace), ctypes.byref(ctypes.c_size_t(workspace.numel() * workspace.element_size()))
+
+
 def compress_k(k, cu_seqlens_k, seqused_k, batch, max_seqlen_k, kernel_size, stride, cu_cmp,
                k_cmp, cmp_begin=None, max_new=0):
     """k [rows_k, h_kv, d] bf16 -> k_cmp [h_kv, c_rows, d] bf16 (in place)."""
@@ -135,14 +143,14 @@ def select_blocks(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_
     rows_q, h_q, d = q.shape
     h_kv, c1_rows, _ = k_c1.shape
     c2_rows = k_c2.shape[1] if k_c2 is not None else 0
-    size = ctypes.c_size_t(workspace.numel() * workspace.element_size())
+    ws, ws_bytes = _ws(workspace)
     _check(load().infllmv2_select_blocks(
         _bf16(q, "q"), _bf16(k_c1, "k_c1"), _bf16(k_c2, "k_c2"), _i32(cu_seqlens_q, "cu_seqlens_q"),
         _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
         _i32(seqused_k, "seqused_k"), _i32(cu_c1, "cu_c1"), _i32(cu_c2, "cu_c2"), batch,
         max_seqlen_q, max_seqlen_k, rows_q, c1_rows, c2_rows, h_q, h_kv, d, block_size, n_init,
         n_local, n_topk, c1[0], c1[1], c2[0], c2[1], pool[0], pool[1], pool[2], softmax_scale,
-        _ptr(workspace), ctypes.byref(size), _i32(block_idx, "block_idx"), _stream()))
+        ws, ws_bytes, _i32(block_idx, "block_idx"), _stream()))
 
 
 def attn_workspace(h_kv, batch, max_seqlen_q, max_seqlen_k, v_seq_stride=0) -> int:
@@ -159,24 +167,23 @@ def sparse_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch
     rows_q, h_q, d = q.shape
     rows_k, h_kv, _ = k.shape
     n_sel = block_idx.shape[-1]
-    size = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
+    ws, ws_bytes = _ws(workspace)
     _check(load().infllmv2_sparse_attn(
         _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _i32(cu_seqlens_q, "cu_seqlens_q"),
         _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
         _i32(seqused_k, "seqused_k"), batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, h_q,
         h_kv, d, block_size, _i32(block_idx, "block_idx"), n_sel, n_init, n_local, softmax_scale,
-        v_seq_stride, _bf16(out, "out"), _ptr(lse), _ptr(workspace), ctypes.byref(size),
-        _stream()))
+        v_seq_stride, _bf16(out, "out"), _ptr(lse), ws, ws_bytes, _stream()))
 
 
 def dense_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch, max_seqlen_q,
                max_seqlen_k, softmax_scale, out, lse=None, workspace=None, v_seq_stride=0):
     rows_q, h_q, d = q.shape
     rows_k, h_kv, _ = k.shape
-    size = ctypes.c_size_t(0 if workspace is None else workspace.numel() * workspace.element_size())
+    ws, ws_bytes = _ws(workspace)
     _check(load().infllmv2_dense_attn(
         _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _i32(cu_seqlens_q, "cu_seqlens_q"),
         _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
         _i32(seqused_k, "seqused_k"), batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, h_q,
-        h_kv, d, softmax_scale, v_seq_stride, _bf16(out, "out"), _ptr(lse), _ptr(workspace),
-        ctypes.byref(size), _stream()))
+        h_kv, d, softmax_scale, v_seq_stride, _bf16(out, "out"), _ptr(lse), ws, ws_bytes,
+        _stream()))
