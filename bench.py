@@ -97,7 +97,7 @@ def cpu_baseline(inp, n, h_q, h_kv, lse_mode, budget_s=15.0):
         t_pre = time.perf_counter() - t0
         rows = 0
         t1 = time.perf_counter()
-        positions = np.linspace(0, n - 1, 64).astype(int)
+        positions = np.linspace(0, n - 1, 2048).astype(int)
         order = np.random.Generator(np.random.PCG64(0)).permutation(positions)
         for t in order:
             t = int(t)

@@ -126,6 +126,7 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_s
   rc = workspace_check(workspace, workspace_bytes, need, &query);
   if (rc || query) return rc;
   if (batch == 0 || max_seqlen_q == 0) return ok();
+  REQUIRE(rows_q >= 1 && rows_k >= 1, INFLLMV2_EINVAL, "rows_q and rows_k must be >= 1");
   REQUIRE(q && k && v && out && cu_seqlens_q && cu_seqlens_k, INFLLMV2_EINVAL, "null tensor pointer");
   REQUIRE(dense || block_idx, INFLLMV2_EINVAL, "null block_idx");
   (void)seqused_q;
