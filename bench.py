@@ -124,6 +124,8 @@ def main():
     ap.add_argument("--lse", choices=["exact", "approx"], default="exact")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--dense-steps", type=int, default=0,
+                    help="also time the dense causal kernel at the same length (context)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -211,6 +213,26 @@ def main():
                      "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
     }
+    if args.dense_steps > 0:
+        print("[bench] dense kernel", file=sys.stderr, flush=True)
+        dplan = P.DensePlan([0], [n], [0], [n], h_kv, cfg)
+        dout = torch.empty_like(q)
+        run_dense = lambda: B.dense_attn(q, k, vt, dplan.cu_q, dplan.used_q, dplan.cu_k,
+                                         dplan.used_k, 1, n, n, cfg.scale(d), dout, None, None,
+                                         v_seq_stride=n)
+        run_dense()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.dense_steps):
+            run_dense()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.dense_steps
+        dflops = 4.0 * d * h_q * (n * (n + 1) / 2)
+        res["dense_attn_ms"] = dms
+        res["dense_attn_tflops"] = dflops / (dms * 1e-3) / 1e12
+        res["sparse_vs_dense_kernel_speedup"] = dms / ms_attn
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, n, h_q, h_kv, args.lse, args.cpu_budget)

@@ -367,32 +367,33 @@ struct Attn {
       // 4. walk the list; the next block's staging loads are in flight while
       //    the current one computes.
       if (n_ent > 0) {
-        // Ring of kRing staged blocks: kRing - 1 are in flight while one is
-        // consumed.  Each stage_issue is 4 loads per wave, so "block u has
-        // landed" means at most 4 * (blocks issued after u) loads outstanding.
-        for (int j = 0; j < kRing - 1 && j < n_ent; ++j) stage_issue(sh.k[j], sh.v[j], sh.ub[j]);
-        for (int u = 0; u < n_ent; ++u) {
-          const int b = __builtin_amdgcn_readfirstlane(sh.ub[u]);
-          const int buf = u % kRing;
-          const int ahead = min(kRing - 2, n_ent - 1 - u);
-          if (ahead >= 2) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
-          } else if (ahead == 1) {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(4));
-          } else {
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-          }
-          __syncthreads();   // block u staged by every wave; block u-1 consumed by every wave
-          if (kBlock * b + kBlock > rk.len) {
-            fix_partial(sh.v[buf], b);
+        // Batches of two blocks: the ring holds the batch being consumed and
+        // the next one in flight; one barrier per batch, so the per-wave load
+        // imbalance of single blocks averages over two.
+        stage_issue(sh.k[0], sh.v[0], sh.ub[0]);
+        if (n_ent > 1) stage_issue(sh.k[1], sh.v[1], sh.ub[1]);
+        for (int u = 0; u < n_ent; u += 2) {
+          const int half = (u >> 1) & 1;
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's part of the batch has landed
+          __syncthreads();                            // ... every wave's; the other half is free
+          const int b0 = __builtin_amdgcn_readfirstlane(sh.ub[u]);
+          const int b1 = u + 1 < n_ent ? __builtin_amdgcn_readfirstlane(sh.ub[u + 1]) : -1;
+          const bool p0 = kBlock * b0 + kBlock > rk.len;
+          const bool p1 = b1 >= 0 && kBlock * b1 + kBlock > rk.len;
+          if (p0 || p1) {
+            if (p0) fix_partial(sh.v[2 * half], b0);
+            if (p1) fix_partial(sh.v[2 * half + 1], b1);
             __syncthreads();
           }
-          if (u + kRing - 1 < n_ent) {
-            const int nb = (u + kRing - 1) % kRing;
-            stage_issue(sh.k[nb], sh.v[nb], sh.ub[u + kRing - 1]);
+          if (u + 2 < n_ent) stage_issue(sh.k[2 * (half ^ 1)], sh.v[2 * (half ^ 1)], sh.ub[u + 2]);
+          if (u + 3 < n_ent) stage_issue(sh.k[2 * (half ^ 1) + 1], sh.v[2 * (half ^ 1) + 1], sh.ub[u + 3]);
+          const uint32_t sh_mask = (1u << kTPW) - 1u;
+          const uint32_t m0 = (__builtin_amdgcn_readfirstlane(sh.um[u]) >> (wave * kTPW)) & sh_mask;
+          if (m0) consume(m0, sh.k[2 * half], sh.v[2 * half], b0);
+          if (b1 >= 0) {
+            const uint32_t m1 = (__builtin_amdgcn_readfirstlane(sh.um[u + 1]) >> (wave * kTPW)) & sh_mask;
+            if (m1) consume(m1, sh.k[2 * half + 1], sh.v[2 * half + 1], b1);
           }
-          const uint32_t msk = (__builtin_amdgcn_readfirstlane(sh.um[u]) >> (wave * kTPW)) & ((1u << kTPW) - 1u);
-          if (msk) consume(msk, sh.k[buf], sh.v[buf], b);
         }
         __syncthreads();   // list and buffers are reused by the next window
       }
