@@ -124,6 +124,9 @@ def main():
     ap.add_argument("--lse", choices=["exact", "approx"], default="exact")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
+                         "kernel of known size, to calibrate HBM byte counters)")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="also time the dense causal kernel at the same length (context)")
     args = ap.parse_args()
@@ -233,6 +236,15 @@ def main():
         res["dense_attn_ms"] = dms
         res["dense_attn_tflops"] = dflops / (dms * 1e-3) / 1e12
         res["sparse_vs_dense_kernel_speedup"] = dms / ms_attn
+    if args.copy_calib_mb > 0:
+        nb = args.copy_calib_mb << 20
+        src = torch.empty(nb, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        res["copy_calib_bytes"] = nb
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, n, h_q, h_kv, args.lse, args.cpu_budget)
