@@ -277,6 +277,8 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   if (batch == 0 || max_seqlen_q == 0) return ok();
   REQUIRE(q && k_c1 && cu_seqlens_q && cu_seqlens_k && cu_c1 && block_idx, INFLLMV2_EINVAL, "null pointer");
   REQUIRE(!approx || cu_c2, INFLLMV2_EINVAL, "cu_c2 required with k_c2");
+  REQUIRE(rows_q >= 1 && c1_rows >= 1 && (!approx || c2_rows >= 1), INFLLMV2_EINVAL,
+          "rows_q and the compressed row counts must be >= 1");
 
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   uint8_t* ws = reinterpret_cast<uint8_t*>(workspace);

@@ -19,9 +19,17 @@
 // lane ends up holding 4 heads of one window: the group sum is 3 in-lane adds
 // plus a reduce-scatter over the four 16-lane rows, after which lane l holds
 // S for window (tile start + l) and a quad max gives the block score.
-// Compressed-key tiles of 64 windows are staged in LDS and shared by the 4
-// waves; each LDS fragment feeds 4 MFMAs (one per token).  Group sizes below
-// 16 pad the head rows with zeros.
+// Compressed-key tiles of 64 windows are staged in LDS (direct global->LDS
+// loads, double-buffered: the next tile lands while this one computes) and
+// shared by the 4 waves; each LDS fragment feeds 4 MFMAs (one per token).
+// Group sizes below 16 pad the head rows with zeros.
+//
+// Pass 1 keeps a per-row offset instead of a per-element running max: the
+// first tile sets it to the exact tile max; afterwards a row's sum is only
+// renormalised (by a power of two) when it exceeds 2^32, and a tile whose sum
+// overflows is redone with its exact max.  Every exponent stays finite and
+// the result is the same log-sum-exp, with one FMA, one exp and one add per
+// score.
 #include "kernels.hpp"
 
 namespace infllmv2 {
@@ -37,21 +45,23 @@ __device__ __forceinline__ int n_visible(int t, int win_kernel, int win_stride, 
   return min(nwin, (t - win_kernel + 1) / win_stride + 1);
 }
 
-// Stage kc[g, cu_c + j0 .. j0+63] into LDS: 64 rows of 256 bytes, 16-byte
-// chunks XOR-swizzled by the row so that 8 consecutive rows read at the same
-// chunk hit distinct banks.
+// Stage kc[g, cu_c + j0 .. j0+63] into LDS with direct global->LDS loads:
+// 64 rows of 256 bytes; each wave writes 4 contiguous 1 KB parts; LDS chunk p
+// of row w receives global chunk p ^ (w & 7), so that 8 consecutive rows read
+// at the same chunk hit distinct banks.  Rows past the sequence's windows
+// read a clamped (valid) row and are masked by visibility.
 __device__ __forceinline__ void stage_windows(uint8_t* lds, const ScoreArgs& a, int g, int64_t c0,
-                                              int j0, int nwin) {
-  const int tid = threadIdx.x;
+                                              int j0, int wave, int lane) {
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
-    const int w = (tid >> 4) + 16 * it;
-    const int ch = tid & 15;
-    const int j = j0 + w;
-    const int64_t row = c0 + j;
-    u32x4 v = zero16();
-    if (j < nwin && row >= 0 && row < a.c_rows) v = ldg16(a.kc + ((int64_t)g * a.c_rows + row) * kHeadDim + 8 * ch);
-    *reinterpret_cast<u32x4*>(lds + w * 256 + ((ch ^ (w & 7)) << 4)) = v;
+    const int part = wave + 4 * it;
+    const int off = part * 1024 + lane * 16;
+    const int w = off >> 8;
+    const int ch = ((off >> 4) & 15) ^ (w & 7);
+    int64_t row = c0 + j0 + w;
+    row = row < a.c_rows ? row : a.c_rows - 1;
+    __builtin_amdgcn_global_load_lds(a.kc + ((int64_t)g * a.c_rows + row) * kHeadDim + 8 * ch,
+                                     (__attribute__((address_space(3))) void*)(lds + part * 1024), 16, 0, 0);
   }
 }
 
@@ -135,65 +145,92 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
     carry[k] = 0.f;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      m[k][r] = -1e30f;
+      m[k][r] = 0.f;
       ssum[k][r] = 0.f;
     }
   }
   const int nv_first = n_visible(t_first, a.win_kernel, a.win_stride, nwin);
+  const int ntiles = (j_end - j_begin + kWT - 1) / kWT;
 
-  for (int jt = j_begin; jt < j_end; jt += kWT) {
-    __syncthreads();
-    stage_windows(lds, a, g, c0, jt, nwin);
-    __syncthreads();
+  stage_windows(lds, a, g, c0, j_begin, wave, lane);
+  for (int it = 0; it < ntiles; ++it) {
+    const int jt = j_begin + it * kWT;
+    const uint8_t* cur = lds + (it & 1) * (kWT * 256);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's part of tile it has landed
+    __syncthreads();                 // ... every wave's; the other buffer is free
+    if (it + 1 < ntiles) stage_windows(lds + ((it + 1) & 1) * (kWT * 256), a, g, c0, jt + kWT, wave, lane);
 
-    floatx4 acc[kTPW][4];
+    bf16x8 bfr[4][4];
 #pragma unroll
-    for (int k = 0; k < kTPW; ++k)
+    for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) acc[k][ct] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int ks = 0; ks < 4; ++ks) bfr[ct][ks] = lds_window_frag(cur, 16 * ct + c16, 4 * ks + q4);
+
+    // Every window of the tile is visible to every token of the tile.
+    const bool full = jt + kWT <= nv_first;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
+    for (int k = 0; k < kTPW; ++k) {
+      floatx4 acc[4];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 b = lds_window_frag(lds, 16 * ct + c16, 4 * ks + q4);
+      for (int ct = 0; ct < 4; ++ct) {
+        acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int k = 0; k < kTPW; ++k) acc[k][ct] = mfma16(qa[k][ks], b, acc[k][ct]);
+        for (int ks = 0; ks < 4; ++ks) acc[ct] = mfma16(qa[k][ks], bfr[ct][ks], acc[ct]);
       }
-    }
-
-    const bool full = jt + kWT <= nv_first;  // every window of the tile visible to every token
-    if (PASS == 1) {
+      bool ok[4];
 #pragma unroll
-      for (int k = 0; k < kTPW; ++k) {
+      for (int ct = 0; ct < 4; ++ct) ok[ct] = full || (jt + 16 * ct + c16 < nv[k]);
+      if (PASS == 1) {
+        if (it == 0) {
+          // First tile: exact offset (every scored token sees window 0).
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            float mt = -__builtin_inff();
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) mt = fmaxf(mt, ok[ct] ? acc[ct][r] : -__builtin_inff());
+            m[k][r] = mt > -__builtin_inff() ? mt : 0.f;
+          }
+        }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          float v[4];
+          const float mc = m[k][r] * a.c;
+          float st = 0.f;
 #pragma unroll
           for (int ct = 0; ct < 4; ++ct) {
-            const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
-            v[ct] = ok ? acc[k][ct][r] : -__builtin_inff();
+            const float e = fast_exp2(fmaf(acc[ct][r], a.c, -mc));
+            st += ok[ct] ? e : 0.f;
           }
-          const float mt = fmaxf(fmaxf(v[0], v[1]), fmaxf(v[2], v[3]));
-          const float mn = fmaxf(m[k][r], mt);
-          const float mc = mn * a.c;
-          float sacc = ssum[k][r] * fast_exp2((m[k][r] - mn) * a.c);
+          if (!(st <= 3.0e38f)) {
+            // Overflow (or NaN): redo this tile's row with its exact max.
+            float mt = m[k][r];
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) sacc += fast_exp2(fmaf(v[ct], a.c, -mc));
-          ssum[k][r] = sacc;
-          m[k][r] = mn;
+            for (int ct = 0; ct < 4; ++ct) mt = fmaxf(mt, ok[ct] ? acc[ct][r] : mt);
+            ssum[k][r] *= fast_exp2((m[k][r] - mt) * a.c);
+            m[k][r] = mt;
+            st = 0.f;
+#pragma unroll
+            for (int ct = 0; ct < 4; ++ct) {
+              const float e = fast_exp2(fmaf(acc[ct][r], a.c, -mt * a.c));
+              st += ok[ct] ? e : 0.f;
+            }
+          }
+          float sn = ssum[k][r] + st;
+          if (sn > 4294967296.f) {
+            // Renormalise by an exact power of two and move the offset.
+            const int e2 = (int)__builtin_amdgcn_logf(sn);   // log2, truncated
+            sn = ldexpf(sn, -e2);
+            m[k][r] += (float)e2 / a.c;
+          }
+          ssum[k][r] = sn;
         }
-      }
-    } else {
-#pragma unroll
-      for (int k = 0; k < kTPW; ++k) {
+      } else {
         float sct[4];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
-          const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
           float sum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sum += fast_exp2(fmaf(acc[k][ct][r], a.c, -Lc[k][r]));
-          sct[ct] = ok ? sum : 0.f;
+          for (int r = 0; r < 4; ++r) sum += fast_exp2(fmaf(acc[ct][r], a.c, -Lc[k][r]));
+          sct[ct] = ok[ct] ? sum : 0.f;
         }
         // Reduce-scatter over the four 16-lane rows: afterwards lane l holds
         // the group sum for window jt + l.
@@ -211,6 +248,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
       }
     }
   }
+  __syncthreads();
 
   if (PASS == 1) {
 #pragma unroll
@@ -237,12 +275,12 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
 }
 
 __global__ __launch_bounds__(256) void score_lse_kernel(ScoreArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWT * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kWT * 256];
   score_body<1>(a, lds);
 }
 
 __global__ __launch_bounds__(256) void score_blocks_kernel(ScoreArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kWT * 256];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kWT * 256];
   score_body<2>(a, lds);
 }
 
