@@ -7,14 +7,19 @@
 // The dense path below the length threshold is the same kernel with every
 // causal block treated as shared.
 //
-// Per workgroup: NW waves x TPW query tokens of one sequence, one KV group.
-//  - Shared phase: blocks that every token of the tile attends (init blocks,
-//    and the local window, which only depends on the token's block) are
-//    staged once in LDS (K as [key][dim], V^T as [dim][key], both
-//    XOR-swizzled) and consumed by all waves.
-//  - Per-token phase: each token's remaining (top-k) blocks come straight
-//    from global memory / L2; the 16 heads of the group form the 16-wide
-//    MFMA tile.
+// Per workgroup: 16 consecutive query tokens of one sequence and one KV group,
+// 8 waves of 2 tokens.  Every block the tokens attend is listed once with a
+// bit mask of its tokens, then consumed in two phases:
+//  - Shared phase: blocks attended by several tokens of the tile (init and
+//    local blocks, popular top-k blocks; dense: every causal block) are
+//    staged once in an LDS ring (K as [key][dim], V^T as [dim][key], both
+//    XOR-swizzled) and consumed by the waves whose tokens attend them, one
+//    workgroup barrier per batch of two blocks.
+//  - Private phase: blocks attended by few tokens are streamed by the waves
+//    that own those tokens, each on its own (K through a per-wave LDS region,
+//    V^T straight into registers), with no workgroup barrier, so a wave that
+//    owns many private blocks does not hold up the others.
+// The 16 heads of the group form the 16-wide MFMA tile.
 // Products are computed transposed: S^T = K Q^T (16 keys x 16 heads per
 // MFMA), then O^T += V^T P^T.  With the key order chosen below, the S^T
 // accumulator of two key tiles is exactly the B operand P^T of the next MFMA,
@@ -44,6 +49,20 @@ __device__ __forceinline__ u32x4 clip_keys(u32x4 v, int first, int limit) {
   return v;
 }
 
+// Opaque copy of a lane value: keeps the compiler from folding lane-constant
+// address offsets into per-load invariants hoisted out of the block loops
+// (which would pin dozens of 64-bit addresses in registers).
+__device__ __forceinline__ int opaque(int v) {
+  int r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
+__device__ __forceinline__ int64_t opaque64(int64_t v) {
+  const int lo = opaque((int)v), hi = opaque((int)(v >> 32));
+  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
 // s_waitcnt immediate: wait until at most n vector-memory loads are
 // outstanding (vmcnt in bits 3:0 and 15:14), no wait on expcnt / lgkmcnt.
 __host__ __device__ constexpr int vmcnt_imm(int n) {
@@ -59,17 +78,21 @@ constexpr int kAttnWaves = 8;                    // waves per workgroup
 constexpr int kTPW = 2;                          // query tokens per wave
 constexpr int kTileTok = kAttnWaves * kTPW;      // 16 tokens per workgroup (one mask bit each)
 constexpr int kThreads = 64 * kAttnWaves;
-constexpr int kWin = 1024;                       // blocks per list window
-constexpr int kRing = 4;                         // staged blocks: 1 computing + 3 in flight
+constexpr int kWin = 2048;                       // blocks per list window (128K keys)
+constexpr int kRing = 4;                         // shared phase: 2 blocks consumed + 2 in flight
+constexpr int kShareMin = 2;                     // tokens attending a block for the shared phase
 
 struct AttnLds {
-  uint8_t k[kRing][64 * 256];   // K block, [key][dim], swizzled (ring of staged blocks)
-  uint8_t v[kRing][128 * 128];  // V^T block, [dim][key], swizzled
+  // Shared phase: slot r holds a K block at ring[r][0] and its V^T at
+  // ring[r][1].  Private phase: wave w owns the 16 KB at (ring[0][0] + 16 KB * w)
+  // for the K block it is streaming.
+  uint8_t ring[kRing][2][64 * 256];
   uint32_t mask[kWin];          // per block of the window: which tile tokens attend it
-  int32_t ub[kWin];             // compacted (block, mask) list
+  int32_t ub[kWin];             // compacted shared-phase (block, mask) list
   uint32_t um[kWin];
-  int32_t wsum[kAttnWaves];
+  int32_t cnt[kWin / kThreads][kAttnWaves];
 };
+static_assert(kRing * 2 * 64 * 256 == kAttnWaves * 64 * 256, "private regions alias the ring");
 
 // One workgroup: 16 consecutive query tokens of one sequence and one KV group.
 // Every block any of them attends (init, local, top-k union; dense: all
@@ -94,12 +117,14 @@ struct Attn {
     float v[4][4];
     float mx = -__builtin_inff();
     if (b == bt[k]) {          // the query's own block: keys after it are masked
-      const int lim = tpos[k] - kBlock * b;
+      // key_of(kt, 4*q4 + r) = 8*q4 + (32*(kt/2) + 4*(kt%2) + r): compare the
+      // lane-free part against the limit shifted by the lane's 8*q4.
+      const int lim = tpos[k] - kBlock * b - 8 * q4;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[kt][r] = key_of(kt, 4 * q4 + r) <= lim ? sacc[kt][r] : -__builtin_inff();
+          v[kt][r] = 32 * (kt >> 1) + 4 * (kt & 1) + r <= lim ? sacc[kt][r] : -__builtin_inff();
           mx = fmaxf(mx, v[kt][r]);
         }
       }
@@ -148,37 +173,60 @@ struct Attn {
     }
   }
 
-  __device__ __forceinline__ const uint16_t* vt_col(int dim) const {
-    return a.vt + (((int64_t)g * kHeadDim + dim) * a.batch + s) * a.vt_ld;
+  // Global addressing of K and V^T blocks: a uniform base per block plus
+  // lane-constant offsets (set once by init_offsets).
+  const uint16_t* kbase;   // K row 0 of this sequence, this KV group
+  const uint16_t* vbase;   // V^T dim 0 of this sequence, this KV group
+  int64_t krow;            // elements between consecutive K rows
+  int64_t vdim;            // elements between consecutive V^T dims
+  int klo[2];              // K staging: lane offset in a 4-row part, per swizzle variant
+  int64_t vlo_stage;       // V^T staging: lane offset in an 8-dim part
+  int64_t vlo_frag;        // V^T fragment loads: lane offset (dim c16, keys 8*q4)
+
+  // K row `row` (relative to the sequence), chunk ch, clamped to the tensor.
+  __device__ __forceinline__ const uint16_t* k_clamped(int row, int ch) const {
+    int64_t r = (int64_t)rk.start + row;
+    r = r < a.rows_k ? r : a.rows_k - 1;
+    return a.k + (r * a.h_kv + g) * kHeadDim + 8 * ch;
+  }
+  // One 1 KB part (4 rows) of K block b into lk + 1024 * part, rows clamped
+  // to the tensor (a block that reaches past its end).
+  __device__ __forceinline__ void stage_k_part(uint8_t* lk, int b, int part) const {
+    const int key = 4 * part + (lane >> 4);
+    __builtin_amdgcn_global_load_lds(k_clamped(kBlock * b + key, (lane & 15) ^ swz_k(key)),
+                                     (__attribute__((address_space(3))) void*)(lk + part * 1024), 16, 0, 0);
+  }
+  // True when every row of block b lies inside the K tensor.
+  __device__ __forceinline__ bool k_inside(int b) const {
+    return (int64_t)rk.start + kBlock * b + kBlock <= a.rows_k;
   }
 
   // Stage block b into LDS with direct global->LDS 16-byte loads (no
   // registers involved): every wave writes two contiguous 1 KB parts of the
   // K tile and two of the V^T tile.  LDS slot (row, chunk p) receives global
-  // chunk p ^ swizzle(row), so the tiles land swizzled.  Rows past the
-  // sequence hold whatever the clamped address reads: K garbage is masked by
-  // causality; a partial V^T block is zeroed by fix_partial().
+  // chunk p ^ swizzle(row), so the tiles land swizzled.  K rows past the
+  // tensor read its last row and rows past the sequence read whatever follows
+  // (both masked by causality); a partial V^T block is zeroed by
+  // fix_partial().
   __device__ __forceinline__ void stage_issue(uint8_t* lk, uint8_t* lv, int b) const {
+    if (k_inside(b)) {
+      const int lo0 = opaque(klo[0]), lo1 = opaque(klo[1]);
+      const uint16_t* base = kbase + (int64_t)(kBlock * b) * krow;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int part = wave + kAttnWaves * j;
-      const int off = part * 1024 + lane * 16;
-      const int key = off >> 8;
-      const int ch = ((off >> 4) & 15) ^ swz_k(key);
-      int64_t row = (int64_t)rk.start + kBlock * b + key;
-      row = row < a.rows_k ? row : a.rows_k - 1;
-      __builtin_amdgcn_global_load_lds(a.k + (row * a.h_kv + g) * kHeadDim + 8 * ch,
-                                       (__attribute__((address_space(3))) void*)(lk + part * 1024), 16, 0, 0);
+      for (int j = 0; j < 2; ++j) {
+        const int part = wave + kAttnWaves * j;
+        __builtin_amdgcn_global_load_lds(base + (int64_t)(4 * part) * krow + ((part & 2) ? lo1 : lo0),
+                                         (__attribute__((address_space(3))) void*)(lk + part * 1024), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) stage_k_part(lk, b, wave + kAttnWaves * j);
     }
+    const uint16_t* pv = vbase + (int64_t)kBlock * b + opaque64(vlo_stage);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int part = wave + kAttnWaves * j;
-      const int off = part * 1024 + lane * 16;
-      const int dim = off >> 7;
-      const int ch = ((off >> 4) & 7) ^ (dim & 7);
-      int64_t first = (int64_t)kBlock * b + 8 * ch;
-      first = first + 8 <= a.vt_ld ? first : a.vt_ld - 8;
-      __builtin_amdgcn_global_load_lds(vt_col(dim) + first,
+      const int part = wave + kAttnWaves * j;   // dims 8*part .. 8*part+7
+      __builtin_amdgcn_global_load_lds(pv + (int64_t)(8 * part) * vdim,
                                        (__attribute__((address_space(3))) void*)(lv + part * 1024), 16, 0, 0);
     }
   }
@@ -198,6 +246,15 @@ struct Attn {
   // V^T fragment (dt, kk) at voff[kk] + 2048*dt.
   int koff[4], voff[2];
   __device__ __forceinline__ void init_offsets() {
+    krow = (int64_t)a.h_kv * kHeadDim;
+    vdim = (int64_t)a.batch * a.vt_ld;
+    kbase = a.k + ((int64_t)rk.start * a.h_kv + g) * kHeadDim;
+    vbase = a.vt + ((int64_t)g * kHeadDim * a.batch + s) * a.vt_ld;
+#pragma unroll
+    for (int v = 0; v < 2; ++v)
+      klo[v] = (lane >> 4) * (int)krow + 8 * ((lane & 15) ^ (((lane >> 4) & 3) | (4 * v)));
+    vlo_stage = (int64_t)(lane >> 3) * vdim + 8 * ((lane & 7) ^ ((lane >> 3) & 7));
+    vlo_frag = (int64_t)c16 * vdim + 8 * q4;
     const int key0 = 8 * (c16 >> 2) + (c16 & 3);
     const int sw = swz_k(key0);   // equal for every key of this lane
 #pragma unroll
@@ -209,29 +266,28 @@ struct Attn {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
   }
 
-  // Block b (staged in lk / lv) for the tokens of this wave whose bit is set
-  // in sel.  All fragment loads of a product are issued before its MFMAs;
-  // the V^T loads are in flight during the softmax.
-  __device__ __forceinline__ void consume(uint32_t sel, const uint8_t* lk, const uint8_t* lv, int b) {
-    floatx4 sacc[kTPW][4];
-    {
-      bf16x8 kf[4][4];
+  // S^T tiles of block b (K staged at lk) for the tokens of this wave in sel.
+  __device__ __forceinline__ void scores(uint32_t sel, const uint8_t* lk, floatx4 (&sacc)[kTPW][4]) const {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+    for (int kt = 0; kt < 4; ++kt) {
+      bf16x8 kf[4];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          kf[kt][ks] = lds16(lk + koff[ks] + 256 * (32 * (kt >> 1) + 4 * (kt & 1)));
+      for (int ks = 0; ks < 4; ++ks) kf[ks] = lds16(lk + koff[ks] + 256 * (32 * (kt >> 1) + 4 * (kt & 1)));
 #pragma unroll
       for (int k = 0; k < kTPW; ++k) {
         if (!((sel >> k) & 1u)) continue;
+        sacc[k][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          sacc[k][kt] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) sacc[k][kt] = mfma16(kf[kt][ks], qb[k][ks], sacc[k][kt]);
-        }
+        for (int ks = 0; ks < 4; ++ks) sacc[k][kt] = mfma16(kf[ks], qb[k][ks], sacc[k][kt]);
       }
     }
+  }
+
+  // Shared phase: block b (staged in lk / lv) for the tokens of this wave
+  // whose bit is set in sel.  The V^T loads are in flight during the softmax.
+  __device__ __forceinline__ void consume(uint32_t sel, const uint8_t* lk, const uint8_t* lv, int b) {
+    floatx4 sacc[kTPW][4];
+    scores(sel, lk, sacc);
     bf16x8 vf[8][2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -248,6 +304,210 @@ struct Attn {
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) o[k][dt] = mfma16(vf[dt][kk], pb[k][kk], o[k][dt]);
+    }
+  }
+
+  // Private phase: this wave alone stages K block b into its LDS region
+  // (16 direct global->LDS loads of 1 KB, same swizzled layout as the ring).
+  __device__ __forceinline__ void issue_k_private(uint8_t* lk, int b) const {
+    if (k_inside(b)) {
+      const int lo0 = opaque(klo[0]), lo1 = opaque(klo[1]);
+      const uint16_t* base = kbase + (int64_t)(kBlock * b) * krow;
+#pragma unroll
+      for (int part = 0; part < 16; ++part)
+        __builtin_amdgcn_global_load_lds(base + (int64_t)(4 * part) * krow + ((part & 2) ? lo1 : lo0),
+                                         (__attribute__((address_space(3))) void*)(lk + part * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int part = 0; part < 16; ++part) stage_k_part(lk, b, part);
+    }
+  }
+  // Private phase: V^T fragments of block b straight into registers
+  // (fragment (dt, kk): dim 16*dt + c16, keys 64*b + 32*kk + 8*q4 .. +8).
+  __device__ __forceinline__ void load_v_private(u32x4 (&vb)[8][2], int b) const {
+    const uint16_t* p = vbase + (int64_t)kBlock * b + opaque64(vlo_frag);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) vb[dt][kk] = ldg16(p + (int64_t)(16 * dt) * vdim + 32 * kk);
+  }
+
+  // Private phase, block b for the tokens of this wave in sel: K from the
+  // wave's region, V^T from registers (keys past the sequence zeroed).
+  __device__ __forceinline__ void consume_private(uint32_t sel, const uint8_t* lk, u32x4 (&vb)[8][2], int b) {
+    if (kBlock * b + kBlock > rk.len) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) vb[dt][kk] = clip_keys(vb[dt][kk], kBlock * b + 32 * kk + 8 * q4, rk.len);
+    }
+    // One token at a time (a private block rarely serves both tokens of the
+    // wave): S^T, softmax and P.V of the first before the second.
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k) {
+      if (!((sel >> k) & 1u)) continue;
+      floatx4 sacc[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        bf16x8 kf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kf[ks] = lds16(lk + koff[ks] + 256 * (32 * (kt >> 1) + 4 * (kt & 1)));
+        sacc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) sacc[kt] = mfma16(kf[ks], qb[k][ks], sacc[kt]);
+      }
+      bf16x8 pb[2];
+      softmax_block(k, b, sacc, pb);
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) o[k][dt] = mfma16(as_bf16x8(vb[dt][kk]), pb[kk], o[k][dt]);
+    }
+  }
+
+  // One window of blocks [w0, w1): build the token masks, run the shared
+  // phase over the popular blocks, then the private phase.
+  __device__ __forceinline__ void window(AttnLds& sh, int w0, int w1, int nq, int pos0, int i0,
+                                         bool dense, int tid) {
+    // 1. init / local (dense: every causal block), by arithmetic.
+    for (int b = w0 + tid; b < w1; b += kThreads) {
+      uint32_t msk = 0;
+      // (a block past the V^T row would mean inconsistent lengths: skipped)
+      for (int tk = 0; tk < nq && kBlock * b + kBlock <= a.vt_ld; ++tk) {
+        const int t = pos0 + i0 + tk;
+        if (t < 0 || (int64_t)rq.start + i0 + tk >= a.rows_q) continue;
+        const int btk = t / kBlock;
+        const bool rel = b <= btk && (dense || b < a.n_init || b >= btk - a.n_local + 1);
+        msk |= (uint32_t)rel << tk;
+      }
+      sh.mask[b - w0] = msk;
+    }
+    __syncthreads();
+    // 2. top-k entries of the tile's tokens (set union; -1, repeats and
+    //    blocks after the token's own are ignored).
+    if (!dense) {
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k) {
+        if (!tval[k]) continue;
+        const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + trow[k]) * a.n_sel;
+        const uint32_t bit = 1u << (wave * kTPW + k);
+        for (int e = lane; e < a.n_sel; e += 64) {
+          const int b = list[e];
+          if (b >= 0 && b <= bt[k] && b >= w0 && b < w1 && kBlock * b + kBlock <= a.vt_ld)
+            atomicOr(&sh.mask[b - w0], bit);
+        }
+      }
+    }
+    __syncthreads();
+    // 3. compact the shared-phase blocks, ascending: entry e = 512*j + tid
+    //    goes to (blocks before round j) + (blocks of earlier waves in
+    //    round j) + (earlier lanes of this wave).
+    const int nblk = w1 - w0;
+    uint64_t bal[kWin / kThreads];
+#pragma unroll
+    for (int j = 0; j < kWin / kThreads; ++j) {
+      const int e = kThreads * j + tid;
+      const uint32_t v = e < nblk ? sh.mask[e] : 0u;
+      bal[j] = __ballot(v != 0u && (dense || __builtin_popcount(v) >= kShareMin));
+      if (lane == 0) sh.cnt[j][wave] = __builtin_popcountll(bal[j]);
+    }
+    __syncthreads();
+    int n_ent = 0;
+#pragma unroll
+    for (int j = 0; j < kWin / kThreads; ++j) {
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kAttnWaves; ++w) {
+        const int c = sh.cnt[j][w];
+        before += w < wave ? c : 0;
+        total += c;
+      }
+      if ((bal[j] >> lane) & 1ull) {
+        const int e = kThreads * j + tid;
+        const int pos = n_ent + before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+        sh.ub[pos] = w0 + e;
+        sh.um[pos] = sh.mask[e];
+      }
+      n_ent += total;
+    }
+    __syncthreads();
+    // 4. shared phase: walk the list; the next batch's staging loads are in
+    //    flight while the current one computes.
+    if (n_ent > 0) {
+      // Batches of two blocks: the ring holds the batch being consumed and
+      // the next one in flight; one barrier per batch, so the per-wave load
+      // imbalance of single blocks averages over two.
+      stage_issue(sh.ring[0][0], sh.ring[0][1], sh.ub[0]);
+      if (n_ent > 1) stage_issue(sh.ring[1][0], sh.ring[1][1], sh.ub[1]);
+      for (int u = 0; u < n_ent; u += 2) {
+        const int half = (u >> 1) & 1;
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's part of the batch has landed
+        __syncthreads();                            // ... every wave's; the other half is free
+        const int b0 = __builtin_amdgcn_readfirstlane(sh.ub[u]);
+        const int b1 = u + 1 < n_ent ? __builtin_amdgcn_readfirstlane(sh.ub[u + 1]) : -1;
+        const bool p0 = kBlock * b0 + kBlock > rk.len;
+        const bool p1 = b1 >= 0 && kBlock * b1 + kBlock > rk.len;
+        if (p0 || p1) {
+          if (p0) fix_partial(sh.ring[2 * half][1], b0);
+          if (p1) fix_partial(sh.ring[2 * half + 1][1], b1);
+          __syncthreads();
+        }
+        if (u + 2 < n_ent) stage_issue(sh.ring[2 * (half ^ 1)][0], sh.ring[2 * (half ^ 1)][1], sh.ub[u + 2]);
+        if (u + 3 < n_ent) stage_issue(sh.ring[2 * (half ^ 1) + 1][0], sh.ring[2 * (half ^ 1) + 1][1], sh.ub[u + 3]);
+        const uint32_t sh_mask = (1u << kTPW) - 1u;
+        const uint32_t m0 = (__builtin_amdgcn_readfirstlane(sh.um[u]) >> (wave * kTPW)) & sh_mask;
+        if (m0) consume(m0, sh.ring[2 * half][0], sh.ring[2 * half][1], b0);
+        if (b1 >= 0) {
+          const uint32_t m1 = (__builtin_amdgcn_readfirstlane(sh.um[u + 1]) >> (wave * kTPW)) & sh_mask;
+          if (m1) consume(m1, sh.ring[2 * half + 1][0], sh.ring[2 * half + 1][1], b1);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();   // the ring becomes the private regions
+    }
+    // 5. private phase: this wave's blocks that stayed out of the shared
+    //    list, ascending, one block in flight (K in the wave's region, V^T
+    //    in registers) while the previous one computes.
+    if (!dense) {
+      uint8_t* region = &sh.ring[0][0][0] + wave * (64 * 256);
+      const uint32_t mine = ((1u << kTPW) - 1u) << (wave * kTPW);
+      int chunk = 0;
+      uint64_t pend = 0;
+      // Next private block of this wave (wave-uniform), or -1.
+      auto next_block = [&](uint32_t& sel) -> int {
+        while (pend == 0) {
+          if (chunk * 64 >= nblk) return -1;
+          const int e = chunk * 64 + lane;
+          const uint32_t v = e < nblk ? sh.mask[e] : 0u;
+          pend = __ballot((v & mine) != 0u && __builtin_popcount(v) < kShareMin);
+          ++chunk;
+        }
+        const int e = (chunk - 1) * 64 + (int)__builtin_ctzll(pend);
+        pend &= pend - 1;
+        sel = (__builtin_amdgcn_readfirstlane(sh.mask[e]) >> (wave * kTPW)) & ((1u << kTPW) - 1u);
+        return w0 + e;
+      };
+      uint32_t sc = 0;
+      int bc = next_block(sc);
+      u32x4 vb[8][2];
+      if (bc >= 0) {
+        issue_k_private(region, bc);
+        load_v_private(vb, bc);
+      }
+      while (bc >= 0) {
+        uint32_t sn = 0;
+        const int bn = next_block(sn);
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // K(bc) in the region, V(bc) in registers
+        consume_private(sc, region, vb, bc);
+        if (bn >= 0) {
+          __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the region's K reads are done
+          issue_k_private(region, bn);
+          load_v_private(vb, bn);
+        }
+        bc = bn;
+        sc = sn;
+      }
     }
   }
 
@@ -299,103 +559,14 @@ struct Attn {
 
     const int nq = min(kTileTok, rq.len - i0);
     const int bt_last = max(0, pos0 + i0 + nq - 1) / kBlock;
-    for (int w0 = 0; w0 <= bt_last; w0 += kWin) {
-      const int w1 = min(bt_last + 1, w0 + kWin);
-      // 1. init / local (dense: every causal block), by arithmetic.
-      for (int b = w0 + tid; b < w1; b += kThreads) {
-        uint32_t msk = 0;
-        for (int tk = 0; tk < nq; ++tk) {
-          const int t = pos0 + i0 + tk;
-          if (t < 0 || (int64_t)rq.start + i0 + tk >= a.rows_q) continue;
-          const int btk = t / kBlock;
-          const bool rel = b <= btk && (dense || b < a.n_init || b >= btk - a.n_local + 1);
-          msk |= (uint32_t)rel << tk;
-        }
-        sh.mask[b - w0] = msk;
-      }
-      __syncthreads();
-      // 2. top-k entries of the tile's tokens (set union; -1, repeats and
-      //    blocks after the token's own are ignored).
-      if (!dense) {
-#pragma unroll
-        for (int k = 0; k < kTPW; ++k) {
-          if (!tval[k]) continue;
-          const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + trow[k]) * a.n_sel;
-          const uint32_t bit = 1u << (wave * kTPW + k);
-          for (int e = lane; e < a.n_sel; e += 64) {
-            const int b = list[e];
-            if (b >= 0 && b <= bt[k] && b >= w0 && b < w1 && kBlock * b + kBlock <= a.vt_ld)
-              atomicOr(&sh.mask[b - w0], bit);
-          }
-        }
-      }
-      __syncthreads();
-      // 3. compact the non-empty blocks, ascending.
-      uint32_t mk[kWin / kThreads];
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < kWin / kThreads; ++j) {
-        const int e = tid * (kWin / kThreads) + j;
-        mk[j] = e < w1 - w0 ? sh.mask[e] : 0u;
-        cnt += mk[j] != 0u;
-      }
-      int incl = cnt;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off);
-        if (lane >= off) incl += v;
-      }
-      if (lane == 63) sh.wsum[wave] = incl;
-      __syncthreads();
-      int wbase = 0, n_ent = 0;
-#pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const int ws = sh.wsum[w];
-        wbase += w < wave ? ws : 0;
-        n_ent += ws;
-      }
-      int pos = wbase + incl - cnt;
-#pragma unroll
-      for (int j = 0; j < kWin / kThreads; ++j) {
-        if (mk[j]) {
-          sh.ub[pos] = w0 + tid * (kWin / kThreads) + j;
-          sh.um[pos] = mk[j];
-          ++pos;
-        }
-      }
-      __syncthreads();
-      // 4. walk the list; the next block's staging loads are in flight while
-      //    the current one computes.
-      if (n_ent > 0) {
-        // Batches of two blocks: the ring holds the batch being consumed and
-        // the next one in flight; one barrier per batch, so the per-wave load
-        // imbalance of single blocks averages over two.
-        stage_issue(sh.k[0], sh.v[0], sh.ub[0]);
-        if (n_ent > 1) stage_issue(sh.k[1], sh.v[1], sh.ub[1]);
-        for (int u = 0; u < n_ent; u += 2) {
-          const int half = (u >> 1) & 1;
-          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's part of the batch has landed
-          __syncthreads();                            // ... every wave's; the other half is free
-          const int b0 = __builtin_amdgcn_readfirstlane(sh.ub[u]);
-          const int b1 = u + 1 < n_ent ? __builtin_amdgcn_readfirstlane(sh.ub[u + 1]) : -1;
-          const bool p0 = kBlock * b0 + kBlock > rk.len;
-          const bool p1 = b1 >= 0 && kBlock * b1 + kBlock > rk.len;
-          if (p0 || p1) {
-            if (p0) fix_partial(sh.v[2 * half], b0);
-            if (p1) fix_partial(sh.v[2 * half + 1], b1);
-            __syncthreads();
-          }
-          if (u + 2 < n_ent) stage_issue(sh.k[2 * (half ^ 1)], sh.v[2 * (half ^ 1)], sh.ub[u + 2]);
-          if (u + 3 < n_ent) stage_issue(sh.k[2 * (half ^ 1) + 1], sh.v[2 * (half ^ 1) + 1], sh.ub[u + 3]);
-          const uint32_t sh_mask = (1u << kTPW) - 1u;
-          const uint32_t m0 = (__builtin_amdgcn_readfirstlane(sh.um[u]) >> (wave * kTPW)) & sh_mask;
-          if (m0) consume(m0, sh.k[2 * half], sh.v[2 * half], b0);
-          if (b1 >= 0) {
-            const uint32_t m1 = (__builtin_amdgcn_readfirstlane(sh.um[u + 1]) >> (wave * kTPW)) & sh_mask;
-            if (m1) consume(m1, sh.k[2 * half + 1], sh.v[2 * half + 1], b1);
-          }
-        }
-        __syncthreads();   // list and buffers are reused by the next window
+    // Sequences up to kWin blocks take one window, without a loop around the
+    // phases (a loop would keep both phases' address registers live at once).
+    if (bt_last < kWin) {
+      window(sh, 0, bt_last + 1, nq, pos0, i0, dense, tid);
+    } else {
+      for (int w0 = 0; w0 <= bt_last; w0 += kWin) {
+        window(sh, w0, min(bt_last + 1, w0 + kWin), nq, pos0, i0, dense, tid);
+        __syncthreads();   // mask, lists and LDS are reused by the next window
       }
     }
 
