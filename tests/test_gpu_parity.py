@@ -334,6 +334,17 @@ def test_128k_sampled(lib, mode):
     _e2e(inp, [n], 32, 2, p, [pos])
 
 
+def test_beyond_128k_two_windows(lib):
+    """n = 133157 (2081 blocks): keys past 128K take the attention kernel
+    that walks the block lists in two windows of 2048 blocks."""
+    say("beyond-128K two-window end-to-end exact")
+    n = 131072 + 2048 + 37
+    p = R.Params(lse_mode="exact")
+    inp = D.make_prefill(11, n, 32, 2, n_needles=32)
+    pos = sample_positions(n, 6, seed=11, must=(131071, 131072 + 100, n - 1))
+    _e2e(inp, [n], 32, 2, p, [pos])
+
+
 def test_varlen_switch(lib):
     """Packed batch of 65536 tokens, lengths from the four buckets; <= 8192
     takes the dense path, longer sequences the sparse path."""

@@ -511,6 +511,7 @@ struct Attn {
     }
   }
 
+  template <bool kMulti>
   __device__ void run(AttnLds& sh) {
     // XCD-aware order: workgroups are dispatched round-robin over the 8
     // XCDs; remap them so each XCD walks a contiguous range of query tiles
@@ -559,10 +560,12 @@ struct Attn {
 
     const int nq = min(kTileTok, rq.len - i0);
     const int bt_last = max(0, pos0 + i0 + nq - 1) / kBlock;
-    // Sequences up to kWin blocks take one window, without a loop around the
-    // phases (a loop would keep both phases' address registers live at once).
-    if (bt_last < kWin) {
-      window(sh, 0, bt_last + 1, nq, pos0, i0, dense, tid);
+    // Keys up to kWin blocks (V^T rows of at most 64 * kWin) take one
+    // window, in a kernel without a loop around the phases (a loop would keep
+    // both phases' address registers live at once).  Blocks past the V^T row
+    // are never attended, so clamping to kWin there loses nothing.
+    if constexpr (!kMulti) {
+      window(sh, 0, min(bt_last + 1, kWin), nq, pos0, i0, dense, tid);
     } else {
       for (int w0 = 0; w0 <= bt_last; w0 += kWin) {
         window(sh, w0, min(bt_last + 1, w0 + kWin), nq, pos0, i0, dense, tid);
@@ -592,17 +595,21 @@ struct Attn {
   }
 };
 
+template <bool kMulti>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds sh;
   Attn st(a);
-  st.run(sh);
+  st.run<kMulti>(sh);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st) {
   dim3 grid((max_seqlen_q + kTileTok - 1) / kTileTok, a.h_kv, a.batch);
-  hipLaunchKernelGGL(attn_kernel, grid, dim3(kThreads), 0, st, a);
+  if (a.vt_ld <= (int64_t)kWin * kBlock)
+    hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kThreads), 0, st, a);
   return hipGetLastError();
 }
 
