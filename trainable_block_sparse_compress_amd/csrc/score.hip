@@ -25,11 +25,11 @@
 // Group sizes below 16 pad the head rows with zeros.
 //
 // Pass 1 keeps a per-row offset instead of a per-element running max: the
-// first tile sets it to the exact tile max; afterwards a row's sum is only
+// first 16 windows set it to their exact max; afterwards a row's sum is only
 // renormalised (by a power of two) when it exceeds 2^32, and a tile whose sum
-// overflows is redone with its exact max.  Every exponent stays finite and
-// the result is the same log-sum-exp, with one FMA, one exp and one add per
-// score.
+// overflows is redone with its exact max (both decided once per tile for the
+// whole wave).  Every exponent stays finite and the result is the same
+// log-sum-exp, with one FMA, one exp and one add per score on full tiles.
 #include "kernels.hpp"
 
 namespace infllmv2 {
@@ -152,6 +152,19 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
   const int nv_first = n_visible(t_first, a.win_kernel, a.win_stride, nwin);
   const int ntiles = (j_end - j_begin + kWT - 1) / kWT;
 
+  // S^T chunk ct (16 windows x 16 heads) of the staged tile for all tokens of
+  // the wave: the four tokens' accumulators are independent MFMA chains.
+  auto chunk = [&](const uint8_t* cur, int ct, floatx4 (&acc)[kTPW]) {
+    bf16x8 b[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) b[ks] = lds_window_frag(cur, 16 * ct + c16, 4 * ks + q4);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k)
+        acc[k] = mfma16(qa[k][ks], b[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[k]);
+  };
+
   stage_windows(lds, a, g, c0, j_begin, wave, lane);
   for (int it = 0; it < ntiles; ++it) {
     const int jt = j_begin + it * kWT;
@@ -160,81 +173,132 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
     __syncthreads();                 // ... every wave's; the other buffer is free
     if (it + 1 < ntiles) stage_windows(lds + ((it + 1) & 1) * (kWT * 256), a, g, c0, jt + kWT, wave, lane);
 
-    bf16x8 bfr[4][4];
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) bfr[ct][ks] = lds_window_frag(cur, 16 * ct + c16, 4 * ks + q4);
-
-    // Every window of the tile is visible to every token of the tile.
+    // Every window of the tile is visible to every token of the tile: no
+    // per-score visibility test.
     const bool full = jt + kWT <= nv_first;
+    if (PASS == 1) {
+      if (it == 0) {
+        // Offset of each row: the max over its visible windows among the
+        // first 16 (every scored token sees window 0).
+        floatx4 acc[kTPW];
+        chunk(cur, 0, acc);
 #pragma unroll
-    for (int k = 0; k < kTPW; ++k) {
-      floatx4 acc[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        acc[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc[ct] = mfma16(qa[k][ks], bfr[ct][ks], acc[ct]);
-      }
-      bool ok[4];
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) ok[ct] = full || (jt + 16 * ct + c16 < nv[k]);
-      if (PASS == 1) {
-        if (it == 0) {
-          // First tile: exact offset (every scored token sees window 0).
+        for (int k = 0; k < kTPW; ++k)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            float mt = -__builtin_inff();
+            const float v = jt + c16 < nv[k] ? acc[k][r] : -__builtin_inff();
+            float mt = v;   // max over the 16 windows: lanes of this 16-lane row
 #pragma unroll
-            for (int ct = 0; ct < 4; ++ct) mt = fmaxf(mt, ok[ct] ? acc[ct][r] : -__builtin_inff());
+            for (int off = 1; off < 16; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
             m[k][r] = mt > -__builtin_inff() ? mt : 0.f;
           }
+      }
+      float st[kTPW][4];
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st[k][r] = 0.f;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 acc[kTPW];
+        chunk(cur, ct, acc);
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k) {
+          const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r] * a.c));
+            st[k][r] += (full || ok) ? e : 0.f;
+          }
         }
+      }
+      // Rare paths, decided once per tile for the whole wave: a tile sum
+      // that overflowed (redo it with the exact tile max), and sums past 2^32
+      // (renormalise by a power of two).
+      bool bad = false, big = false;
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const float mc = m[k][r] * a.c;
-          float st = 0.f;
-#pragma unroll
-          for (int ct = 0; ct < 4; ++ct) {
-            const float e = fast_exp2(fmaf(acc[ct][r], a.c, -mc));
-            st += ok[ct] ? e : 0.f;
-          }
-          if (!(st <= 3.0e38f)) {
-            // Overflow (or NaN): redo this tile's row with its exact max.
-            float mt = m[k][r];
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) mt = fmaxf(mt, ok[ct] ? acc[ct][r] : mt);
-            ssum[k][r] *= fast_exp2((m[k][r] - mt) * a.c);
-            m[k][r] = mt;
-            st = 0.f;
-#pragma unroll
-            for (int ct = 0; ct < 4; ++ct) {
-              const float e = fast_exp2(fmaf(acc[ct][r], a.c, -mt * a.c));
-              st += ok[ct] ? e : 0.f;
-            }
-          }
-          float sn = ssum[k][r] + st;
-          if (sn > 4294967296.f) {
-            // Renormalise by an exact power of two and move the offset.
-            const int e2 = (int)__builtin_amdgcn_logf(sn);   // log2, truncated
-            sn = ldexpf(sn, -e2);
-            m[k][r] += (float)e2 / a.c;
-          }
-          ssum[k][r] = sn;
+          bad |= !(st[k][r] <= 3.0e38f);
+          big |= ssum[k][r] + st[k][r] > 4294967296.f;
         }
-      } else {
-        float sct[4];
+      if (__ballot(bad) != 0) {
+        float mt[kTPW][4];
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) mt[k][r] = m[k][r];
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct) {
+          floatx4 acc[kTPW];
+          chunk(cur, ct, acc);
+#pragma unroll
+          for (int k = 0; k < kTPW; ++k) {
+            const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) mt[k][r] = fmaxf(mt[k][r], ok ? acc[k][r] : mt[k][r]);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            ssum[k][r] *= fast_exp2((m[k][r] - mt[k][r]) * a.c);
+            m[k][r] = mt[k][r];
+            st[k][r] = 0.f;
+          }
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          floatx4 acc[kTPW];
+          chunk(cur, ct, acc);
+#pragma unroll
+          for (int k = 0; k < kTPW; ++k) {
+            const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r] * a.c));
+              st[k][r] += ok ? e : 0.f;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ssum[k][r] += st[k][r];
+      if (__ballot(big) != 0) {
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float sn = ssum[k][r];
+            if (sn > 4294967296.f) {
+              const int e2 = (int)__builtin_amdgcn_logf(sn);   // log2, truncated
+              ssum[k][r] = ldexpf(sn, -e2);
+              m[k][r] += (float)e2 / a.c;
+            }
+          }
+      }
+    } else {
+      float sct[kTPW][4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        floatx4 acc[kTPW];
+        chunk(cur, ct, acc);
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k) {
           float sum = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sum += fast_exp2(fmaf(acc[ct][r], a.c, -Lc[k][r]));
-          sct[ct] = ok[ct] ? sum : 0.f;
+          for (int r = 0; r < 4; ++r) sum += fast_exp2(fmaf(acc[k][r], a.c, -Lc[k][r]));
+          sct[k][ct] = (full || jt + 16 * ct + c16 < nv[k]) ? sum : 0.f;
         }
+      }
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k) {
         // Reduce-scatter over the four 16-lane rows: afterwards lane l holds
         // the group sum for window jt + l.
-        const float S = rs_x16(rs_x32(sct[0], sct[2]), rs_x32(sct[1], sct[3]));
+        const float S = rs_x16(rs_x32(sct[k][0], sct[k][2]), rs_x32(sct[k][1], sct[k][3]));
         const float q1 = fmaxf(S, __shfl_xor(S, 1));
         const float qm = fmaxf(q1, __shfl_xor(q1, 2));     // windows 4b .. 4b+3
         float prev = __shfl_up(S, 1);                        // window 4b-1
@@ -274,12 +338,12 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
   }
 }
 
-__global__ __launch_bounds__(256) void score_lse_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256, 2) void score_lse_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kWT * 256];
   score_body<1>(a, lds);
 }
 
-__global__ __launch_bounds__(256) void score_blocks_kernel(ScoreArgs a) {
+__global__ __launch_bounds__(256, 2) void score_blocks_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kWT * 256];
   score_body<2>(a, lds);
 }
