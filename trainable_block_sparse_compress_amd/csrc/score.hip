@@ -30,6 +30,8 @@
 // overflows is redone with its exact max (both decided once per tile for the
 // whole wave).  Every exponent stays finite and the result is the same
 // log-sum-exp, with one FMA, one exp and one add per score on full tiles.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace infllmv2 {
@@ -39,6 +41,13 @@ namespace {
 constexpr int kQT = 16;      // query tokens per workgroup
 constexpr int kTPW = 4;      // tokens per wave
 constexpr int kWT = 64;      // windows per tile
+
+// DPP move of a float: lane i takes src from the lane the control selects;
+// lanes without a source keep `old`.
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float old, float src) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(src), kCtrl, 0xF, 0xF, false));
+}
 
 __device__ __forceinline__ int n_visible(int t, int win_kernel, int win_stride, int nwin) {
   if (t < win_kernel - 1) return 0;
@@ -194,24 +203,27 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
           }
       }
       float st[kTPW][4];
+      // One straight-line body per case: full tiles carry no visibility select.
+      auto tile_sums = [&](auto full_c) {
+        constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-      for (int k = 0; k < kTPW; ++k)
+        for (int ct = 0; ct < 4; ++ct) {
+          floatx4 acc[kTPW];
+          chunk(cur, ct, acc);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st[k][r] = 0.f;
+          for (int k = 0; k < kTPW; ++k) {
+            const bool ok = kFull || (jt + 16 * ct + c16 < nv[k]);
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        floatx4 acc[kTPW];
-        chunk(cur, ct, acc);
-#pragma unroll
-        for (int k = 0; k < kTPW; ++k) {
-          const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r] * a.c));
-            st[k][r] += (full || ok) ? e : 0.f;
+            for (int r = 0; r < 4; ++r) {
+              float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r] * a.c));
+              if (!kFull) e = ok ? e : 0.f;
+              st[k][r] = ct == 0 ? e : st[k][r] + e;
+            }
           }
         }
-      }
+      };
+      if (full) tile_sums(std::true_type{});
+      else tile_sums(std::false_type{});
       // Rare paths, decided once per tile for the whole wave: a tile sum
       // that overflowed (redo it with the exact tile max), and sums past 2^32
       // (renormalise by a power of two).
@@ -282,28 +294,34 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
       }
     } else {
       float sct[kTPW][4];
+      auto tile_probs = [&](auto full_c) {
+        constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        floatx4 acc[kTPW];
-        chunk(cur, ct, acc);
+        for (int ct = 0; ct < 4; ++ct) {
+          floatx4 acc[kTPW];
+          chunk(cur, ct, acc);
 #pragma unroll
-        for (int k = 0; k < kTPW; ++k) {
-          float sum = 0.f;
+          for (int k = 0; k < kTPW; ++k) {
+            float sum = fast_exp2(fmaf(acc[k][0], a.c, -Lc[k][0]));
 #pragma unroll
-          for (int r = 0; r < 4; ++r) sum += fast_exp2(fmaf(acc[k][r], a.c, -Lc[k][r]));
-          sct[k][ct] = (full || jt + 16 * ct + c16 < nv[k]) ? sum : 0.f;
+            for (int r = 1; r < 4; ++r) sum += fast_exp2(fmaf(acc[k][r], a.c, -Lc[k][r]));
+            sct[k][ct] = (kFull || jt + 16 * ct + c16 < nv[k]) ? sum : 0.f;
+          }
         }
-      }
+      };
+      if (full) tile_probs(std::true_type{});
+      else tile_probs(std::false_type{});
 #pragma unroll
       for (int k = 0; k < kTPW; ++k) {
         // Reduce-scatter over the four 16-lane rows: afterwards lane l holds
         // the group sum for window jt + l.
         const float S = rs_x16(rs_x32(sct[k][0], sct[k][2]), rs_x32(sct[k][1], sct[k][3]));
-        const float q1 = fmaxf(S, __shfl_xor(S, 1));
-        const float qm = fmaxf(q1, __shfl_xor(q1, 2));     // windows 4b .. 4b+3
-        float prev = __shfl_up(S, 1);                        // window 4b-1
-        if (lane == 0) prev = carry[k];
-        carry[k] = __shfl(S, 63);
+        // Quad max (windows 4b .. 4b+3) and the window before each quad
+        // (4b-1; lane 0 takes the previous tile's last window) via DPP.
+        const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));          // quad_perm 1,0,3,2
+        const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));       // quad_perm 2,3,0,1
+        const float prev = dpp_f32<0x138>(carry[k], S);          // wave_shr:1
+        carry[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 63));
         if (need[k] && (lane & 3) == 0) {
           const int b = (jt >> 2) + (lane >> 2);
           if (b >= a.n_init && b <= bt[k] - a.n_local && b < a.bs_ld)
