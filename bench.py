@@ -218,7 +218,7 @@ def main():
     }
     if args.dense_steps > 0:
         print("[bench] dense kernel", file=sys.stderr, flush=True)
-        dplan = P.DensePlan([0], [n], [0], [n], h_kv, cfg)
+        dplan = P.DensePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
         dout = torch.empty_like(q)
         run_dense = lambda: B.dense_attn(q, k, vt, dplan.cu_q, dplan.used_q, dplan.cu_k,
                                          dplan.used_k, 1, n, n, cfg.scale(d), dout, None, None,

@@ -160,12 +160,12 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
  *   out[t, h] = sum_{u in T} softmax_u(softmax_scale * q[t, h] . k[u, g]) v[u, g],
  *   T = {u <= position(t) : floor(u / 64) in init(t) ∪ local(t) ∪ block_idx[g, t, :]}
  *
- * with init(t) = {0..n_init-1} and local(t) = {b_t-n_local+1..b_t}.  Each
- * row of block_idx is ascending; entries equal to -1, repeating the previous
- * entry, or later than b_t are skipped.  The output of
- * infllmv2_select_blocks can be passed as is, and any other ascending block
- * list works with n_init = n_local = 0.  A row that attends no key gets
- * out = 0 and lse = -inf.
+ * with init(t) = {0..n_init-1} and local(t) = {b_t-n_local+1..b_t}.  A row
+ * of block_idx is read as a set: its order does not matter, and entries
+ * equal to -1, repeated, or later than b_t are skipped.  The output of
+ * infllmv2_select_blocks can be passed as is, and any other block list works
+ * with n_init = n_local = 0.  A row that attends no key gets out = 0 and
+ * lse = -inf.
  *
  *   q, out     bf16 [rows_q, h_q, head_dim]
  *   k          bf16 [rows_k, h_kv, head_dim]
@@ -176,8 +176,13 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
  *              must be a multiple of 64; columns past len_k(s) are never used)
  *   block_idx  int32 [h_kv, rows_q, n_sel]
  *   lse_out    float [h_q, rows_q] natural-log softmax normaliser, or NULL
- *   workspace  size from a query with the same shape arguments (0 bytes when
- *              v_seq_stride > 0)
+ *   workspace  size from a query with the same shape arguments: the
+ *              transposed V (only when v_seq_stride == 0) and, for launches
+ *              with few query tiles (fewer than 512 tiles of 16 rows per KV
+ *              group, at most 64 query rows per sequence, at most 1024 list
+ *              + init + local entries per row: decode), the split-K partials
+ *              of about 8 KB per (row, KV group, split).  Zero bytes when
+ *              neither applies.
  */
 int infllmv2_sparse_attn(const void* q, const void* k, const void* v,
                          const int32_t* cu_seqlens_q, const int32_t* seqused_q,

@@ -14,6 +14,12 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "infllmv2.h")
 
 OK, EINVAL, EUNSUP, EWS = 0, -1, -2, -3
+# floats of one split-K partial: O[16][128], l[16], m[16]
+PART_FLOATS = 16 * 128 + 32
+
+
+def align(x):
+    return (x + 255) // 256 * 256
 
 
 @pytest.fixture(scope="module")
@@ -91,7 +97,6 @@ def test_select_blocks_workspace_size(lib):
     lse = h_q * rows * 4
     bs_ld = ((n // 64 + 3) // 4) * 4
     bs = h_kv * rows * bs_ld * 4
-    align = lambda x: (x + 255) // 256 * 256
     assert size == align(lse) + align(bs)
 
 
@@ -111,8 +116,19 @@ def test_attention_validation_and_workspace(lib):
     rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
                                  32, 2, 128, 0.088, 100, None, None, None, ctypes.byref(size), None)
     assert rc == EINVAL  # v_seq_stride not a multiple of 64
+    # one tiny sequence: split-K partials only (V given transposed), one split
     rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
                                  32, 2, 128, 0.088, 64, None, None, None, ctypes.byref(size), None)
+    assert rc == OK and size.value == align(10 * 2 * 1 * PART_FLOATS * 4)
+    # decode-like: 16 sequences x 1 query over 128K keys, 96 blocks -> 16 splits
+    rc = lib.infllmv2_sparse_attn(None, None, None, None, None, None, None, 16, 1, 131072, 16, 0,
+                                  32, 2, 128, 64, None, 96, 1, 32, 0.088, 131072, None, None, None,
+                                  ctypes.byref(size), None)
+    assert rc == OK and size.value == align(16 * 2 * 16 * PART_FLOATS * 4)
+    # many query tiles: the tile kernel, no partials
+    rc = lib.infllmv2_sparse_attn(None, None, None, None, None, None, None, 1, 131072, 131072,
+                                  131072, 0, 32, 2, 128, 64, None, 96, 1, 32, 0.088, 131072, None,
+                                  None, None, ctypes.byref(size), None)
     assert rc == OK and size.value == 0
     rc = lib.infllmv2_sparse_attn(None, None, None, None, None, None, None, 1, 10, 10, 10, 10,
                                   32, 2, 128, 64, None, 0, 1, 32, 0.088, 0, None, None, None,
@@ -154,7 +170,8 @@ def test_switch_partition_and_window_counts():
 def test_no_workspace_is_not_a_size_query(lib):
     """A NULL workspace with a NULL size pointer must take the launch path
     (here: rejected for NULL tensors), never the size-query path."""
-    rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 64, 64, 64, 64,
-                                 32, 2, 128, 0.088, 64, None, None, None, None, None)
+    # (enough query tiles for the tile kernel, V given transposed: no workspace needed)
+    rc = lib.infllmv2_dense_attn(None, None, None, None, None, None, None, 1, 8192, 8192, 8192,
+                                 8192, 32, 2, 128, 0.088, 8192, None, None, None, None, None)
     assert rc == EINVAL
     assert B._ws(None) == (None, None)

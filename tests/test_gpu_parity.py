@@ -103,7 +103,7 @@ def test_dense_attention(lib, lengths, h_q, h_kv):
     cfg = P.SparseConfig()
     out = torch.empty_like(q)
     lse = torch.empty((h_q, q.shape[0]), dtype=torch.float32, device="cuda")
-    P.DensePlan(st, lengths, st, lengths, h_kv, cfg).run(q, k, v, out, lse)
+    P.DensePlan(st, lengths, st, lengths, sum(lengths), h_q, h_kv, cfg).run(q, k, v, out, lse)
     torch.cuda.synchronize()
     of, lf = to_f64(out), lse.cpu().numpy()
     G, scale = h_q // h_kv, 1 / math.sqrt(128)
@@ -160,7 +160,9 @@ def test_sparse_attention_given_lists(lib, lengths, h_q, h_kv, sel):
     st = _starts(lengths)
     out = torch.empty_like(q)
     lse = torch.empty((h_q, q.shape[0]), dtype=torch.float32, device="cuda")
-    ws = torch.empty(max(1, B.attn_workspace(h_kv, len(lengths), max(lengths), max(lengths))),
+    ws = torch.empty(max(1, B.attn_workspace(h_q, h_kv, len(lengths), max(lengths), max(lengths),
+                                             sum(lengths), n_sel=idx.shape[-1], n_init=p.n_init,
+                                             n_local=p.n_local)),
                      dtype=torch.uint8, device="cuda")
     B.sparse_attn(q, k, v, i32(st), i32(lengths), i32(st), i32(lengths), len(lengths),
                   max(lengths), max(lengths), idx, p.n_init, p.n_local, 1 / math.sqrt(128), out,
@@ -180,6 +182,67 @@ def test_sparse_attention_given_lists(lib, lengths, h_q, h_kv, sel):
             assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (s, t, ma, rr)
             assert np.abs(lf[:, st[s] + t] - l_ref).max() < 1e-3, (s, t)
     say(f"  max abs err {worst:.3e}")
+
+
+@pytest.mark.parametrize("h_q,h_kv", [(32, 2), (8, 1)])
+def test_split_path_short_queries(lib, h_q, h_kv):
+    """Few query tiles (decode-like: 5, 1 and 3 queries at the end of 3000,
+    4100 and 700 keys) take the split-K kernels.  Lists carry repeats, -1
+    pads and blocks after the query's own, in scrambled order; both the
+    sparse and the dense entry point are checked against the oracle."""
+    say(f"split path h_q={h_q} h_kv={h_kv}")
+    klens, qlens = [3000, 4100, 700], [5, 1, 3]
+    inp = D.make_prefill(31, klens, h_q, h_kv)
+    kst = _starts(klens)
+    qrows = [kst[s] + klens[s] - qlens[s] + i for s in range(3) for i in range(qlens[s])]
+    qst = _starts(qlens)
+    q = to_dev(np.ascontiguousarray(inp.q[qrows]))
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    rng = np.random.Generator(np.random.PCG64(7))
+    n_sel = 40
+    idx = np.full((h_kv, len(qrows), n_sel), -1, dtype=np.int32)
+    want = {}
+    for s in range(3):
+        for i in range(qlens[s]):
+            t = klens[s] - qlens[s] + i
+            bt = t // 64
+            for g in range(h_kv):
+                pick = rng.choice(bt + 1, size=min(bt + 1, 20), replace=False).tolist()
+                extra = pick[:5] + [-1, -1, bt + 1 + int(rng.integers(0, 3))]
+                entries = pick + extra
+                rng.shuffle(entries)
+                idx[g, qst[s] + i, :len(entries)] = entries
+                want[(s, i, g)] = sorted(set(b for b in pick if 0 <= b <= bt))
+    idx_t = torch.from_numpy(idx).cuda()
+    scale = 1 / math.sqrt(128)
+    args = (i32(qst), i32(qlens), i32(kst), i32(klens), 3, max(qlens), max(klens))
+    for dense in (False, True):
+        ws_bytes = B.attn_workspace(h_q, h_kv, 3, max(qlens), max(klens), len(qrows),
+                                    n_sel=0 if dense else n_sel)
+        ws = torch.empty(max(1, ws_bytes), dtype=torch.uint8, device="cuda")
+        out = torch.full_like(q, float("nan"))
+        lse = torch.empty((h_q, len(qrows)), dtype=torch.float32, device="cuda")
+        if dense:
+            B.dense_attn(q, k, v, *args, scale, out, lse, ws)
+        else:
+            B.sparse_attn(q, k, v, *args, idx_t, 0, 0, scale, out, lse, ws)
+        torch.cuda.synchronize()
+        of, lf = to_f64(out), lse.cpu().numpy()
+        p = R.Params()
+        for s in range(3):
+            Ks = R.as_f64(inp.k[kst[s]:kst[s] + klens[s]])
+            Vs = R.as_f64(inp.v[kst[s]:kst[s] + klens[s]])
+            for i in range(qlens[s]):
+                t = klens[s] - qlens[s] + i
+                qv = inp.q[kst[s] + t]
+                if dense:
+                    o_ref, l_ref = R.dense_token(qv, t, Ks, Vs, h_q // h_kv, scale)
+                else:
+                    o_ref, l_ref = R.attend_token(qv, t, Ks, Vs, [want[(s, i, g)] for g in range(h_kv)],
+                                                  h_q // h_kv, p)
+                ma, rr = attn_errors(of[qst[s] + i], o_ref)
+                assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (dense, s, i, ma, rr)
+                assert np.abs(lf[:, qst[s] + i] - l_ref).max() < 1e-3, (dense, s, i)
 
 
 # ----------------------------------------------------------------------------
@@ -294,7 +357,7 @@ def test_tiny_full_budget_equals_dense(lib):
         assert list(idx[0, t][:t // 64 + 1]) == list(range(t // 64 + 1))
     q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
     dense = torch.empty_like(q)
-    P.DensePlan([0], [4096], [0], [4096], h_kv, P.SparseConfig()).run(q, k, v, dense)
+    P.DensePlan([0], [4096], [0], [4096], 4096, h_q, h_kv, P.SparseConfig()).run(q, k, v, dense)
     Qf, Kf, Vf = R.as_f64(inp.q), R.as_f64(inp.k), R.as_f64(inp.v)
     ref = R.dense_prefill(Qf, Kf, Vf, 2, 1 / math.sqrt(128), positions=range(0, 4096, 5))
     o_ref = np.stack([ref[t][0] for t in ref])

@@ -153,11 +153,21 @@ def select_blocks(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_
         ws, ws_bytes, _i32(block_idx, "block_idx"), _stream()))
 
 
-def attn_workspace(h_kv, batch, max_seqlen_q, max_seqlen_k, v_seq_stride=0) -> int:
+def attn_workspace(h_q, h_kv, batch, max_seqlen_q, max_seqlen_k, rows_q, v_seq_stride=0,
+                   n_sel=0, n_init=0, n_local=0) -> int:
+    """Workspace bytes of sparse_attn (n_sel > 0) or dense_attn (n_sel == 0)
+    for these sizes: the V transposition (v_seq_stride == 0) and, for
+    launches with few query tiles, the split-K partials."""
     size = ctypes.c_size_t(0)
-    _check(load().infllmv2_dense_attn(
-        None, None, None, None, None, None, None, batch, max_seqlen_q, max_seqlen_k, 0, 0,
-        h_kv, h_kv, 128, 1.0, v_seq_stride, None, None, None, ctypes.byref(size), None))
+    if n_sel > 0:
+        _check(load().infllmv2_sparse_attn(
+            None, None, None, None, None, None, None, batch, max_seqlen_q, max_seqlen_k, rows_q, 0,
+            h_q, h_kv, 128, 64, None, n_sel, n_init, n_local, 1.0, v_seq_stride, None, None, None,
+            ctypes.byref(size), None))
+    else:
+        _check(load().infllmv2_dense_attn(
+            None, None, None, None, None, None, None, batch, max_seqlen_q, max_seqlen_k, rows_q, 0,
+            h_q, h_kv, 128, 1.0, v_seq_stride, None, None, None, ctypes.byref(size), None))
     return size.value
 
 

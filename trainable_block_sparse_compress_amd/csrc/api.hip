@@ -72,6 +72,25 @@ size_t vt_bytes(int h_kv, int batch, int max_seqlen_k) {
   return align_up((size_t)h_kv * kHeadDim * (size_t)batch * (size_t)ld * 2);
 }
 
+// Launches with fewer query tiles than this take the split-K path.
+constexpr int64_t kSplitTileLimit = 512;
+constexpr int kSplitTargetWgs = 512;
+constexpr int kSplitMaxSplits = 64;
+
+// Split count of the split-K attention path, or 0 for the tile kernel.
+int attn_splits(int64_t rows_q, int batch, int max_seqlen_q, int max_seqlen_k, int h_kv, bool dense,
+                int n_sel, int n_init, int n_local) {
+  const int64_t tiles = ceil_div(std::max(1, max_seqlen_q), 16) * h_kv * std::max(1, batch);
+  if (tiles >= kSplitTileLimit || max_seqlen_q > 64 || rows_q > kMaxGrid || rows_q < 1) return 0;
+  if (!dense && (int64_t)n_sel + n_init + n_local > kSplitMaxSel) return 0;
+  const int64_t blocks = dense ? ceil_div(std::max(1, max_seqlen_k), kBlock)
+                               : std::min<int64_t>((int64_t)n_sel + n_init + n_local,
+                                                   ceil_div(std::max(1, max_seqlen_k), kBlock));
+  const int64_t want = ceil_div(kSplitTargetWgs, rows_q * h_kv);
+  const int64_t cap = std::max<int64_t>(1, blocks / 4);   // at least one block per wave
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, (int64_t)kSplitMaxSplits}));
+}
+
 int workspace_check(void* ws, size_t* bytes, size_t need, bool* query) {
   *query = false;
   if (ws == nullptr && bytes != nullptr) {
@@ -121,7 +140,12 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_s
     REQUIRE(v_seq_stride >= round_up(max_seqlen_k, kBlock), INFLLMV2_EINVAL,
             "v_seq_stride %lld < max_seqlen_k rounded to 64", (long long)v_seq_stride);
   }
-  const size_t need = v_seq_stride > 0 ? 0 : vt_bytes(h_kv, batch, max_seqlen_k);
+  const int splits = attn_splits(rows_q, batch, max_seqlen_q, max_seqlen_k, h_kv, dense, n_sel,
+                                 n_init, n_local);
+  const size_t vt_need = v_seq_stride > 0 ? 0 : vt_bytes(h_kv, batch, max_seqlen_k);
+  const size_t part_need =
+      splits > 0 ? align_up((size_t)rows_q * h_kv * splits * kPartFloats * sizeof(float)) : 0;
+  const size_t need = vt_need + part_need;
   bool query = false;
   rc = workspace_check(workspace, workspace_bytes, need, &query);
   if (rc || query) return rc;
@@ -174,7 +198,12 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_s
   a.c = softmax_scale * 1.4426950408889634f;
   a.out = reinterpret_cast<uint16_t*>(out);
   a.lse = lse_out;
-  rc = hip_status(launch_attention(a, max_seqlen_q, st), "attention launch");
+  if (splits > 0) {
+    float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(workspace) + vt_need);
+    rc = hip_status(launch_attention_split(a, rows_q, splits, part, st), "split attention launch");
+  } else {
+    rc = hip_status(launch_attention(a, max_seqlen_q, st), "attention launch");
+  }
   if (rc) return rc;
   return ok();
 }

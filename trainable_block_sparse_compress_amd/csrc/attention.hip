@@ -614,3 +614,294 @@ hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st)
 }
 
 }  // namespace infllmv2
+
+// ---------------------------------------------------------------------------
+// Split-K path.  With few query tiles (decode: one token per sequence) the
+// tile kernel above would leave most of the chip idle, each workgroup
+// walking a whole block list alone.  Here a workgroup takes one query row,
+// one KV group and one range of the row's (deduplicated, ascending) block
+// set; its four waves take every fourth block of the range straight from
+// global memory into registers, merge their online-softmax states in LDS and
+// write one partial.  The merge kernel combines the partials of a row.
+// ---------------------------------------------------------------------------
+namespace infllmv2 {
+namespace {
+
+constexpr int kSplitWaves = 4;
+constexpr int kSplitThreads = 64 * kSplitWaves;
+
+struct SplitLds {
+  int32_t list[kSplitMaxSel];
+  int32_t cnt[kSplitMaxSel / kSplitThreads][kSplitWaves];
+  float pm[kSplitWaves][16];   // running max per head (the lanes of a head share it)
+  float pl[kSplitWaves][16];
+  float po[kSplitWaves][16 * kHeadDim];
+};
+
+// Sequence holding packed query row `row` (cu_q non-decreasing), or -1.
+__device__ __forceinline__ int seq_of_row(const AttnArgs& a, int64_t row) {
+  int lo = 0, hi = a.batch - 1;
+  if (hi < 0) return -1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_q[mid] <= row) lo = mid;
+    else hi = mid - 1;
+  }
+  const SeqRange r = seq_range(a.cu_q, a.used_q, lo);
+  return (row >= r.start && row < (int64_t)r.start + r.len) ? lo : -1;
+}
+
+__global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a, int splits, float* part) {
+  __shared__ __attribute__((aligned(16))) SplitLds sh;
+  const int sp = blockIdx.x, g = blockIdx.y;
+  const int64_t row = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int s = seq_of_row(a, row);
+  if (s < 0) return;
+  const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
+  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
+  const int t = rk.len - rq.len + (int)(row - rq.start);
+  if (t < 0) return;
+  const int bt = t / kBlock;
+  const bool dense = a.bidx == nullptr;
+  const int nvt = (int)(a.vt_ld / kBlock);   // blocks inside a V^T row
+
+  // The row's block set, ascending and without repeats.
+  int nb;
+  if (dense) {
+    nb = min(bt + 1, nvt);
+  } else {
+    // Candidates: the list, then the init blocks, then the local blocks.
+    const int n_cand = a.n_sel + a.n_init + a.n_local;
+    int p2 = 1;
+    while (p2 < n_cand) p2 <<= 1;
+    const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + row) * a.n_sel;
+    for (int i = tid; i < p2; i += kSplitThreads) {
+      int b = -1;
+      if (i < a.n_sel) b = list[i];
+      else if (i < a.n_sel + a.n_init) b = i - a.n_sel;
+      else if (i < n_cand) b = bt - (i - a.n_sel - a.n_init);
+      sh.list[i] = (b >= 0 && b <= bt && b < nvt) ? b : 0x7fffffff;
+    }
+    __syncthreads();
+    for (int k = 2; k <= p2; k <<= 1) {          // bitonic sort
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < p2; i += kSplitThreads) {
+          const int pi = i ^ j;
+          if (pi > i) {
+            const int x = sh.list[i], y = sh.list[pi];
+            if (((i & k) == 0) == (x > y)) {
+              sh.list[i] = y;
+              sh.list[pi] = x;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    int vals[kSplitMaxSel / kSplitThreads];
+    uint64_t bal[kSplitMaxSel / kSplitThreads];
+#pragma unroll
+    for (int j = 0; j < kSplitMaxSel / kSplitThreads; ++j) {
+      const int i = kSplitThreads * j + tid;
+      const int v = i < p2 ? sh.list[i] : 0x7fffffff;
+      const bool keep = v != 0x7fffffff && (i == 0 || sh.list[i - 1] != v);
+      vals[j] = v;
+      bal[j] = __ballot(keep);
+      if (lane == 0) sh.cnt[j][wave] = __builtin_popcountll(bal[j]);
+    }
+    __syncthreads();
+    nb = 0;
+#pragma unroll
+    for (int j = 0; j < kSplitMaxSel / kSplitThreads; ++j) {
+      int before = 0, total = 0;
+#pragma unroll
+      for (int w = 0; w < kSplitWaves; ++w) {
+        const int c = sh.cnt[j][w];
+        before += w < wave ? c : 0;
+        total += c;
+      }
+      if ((bal[j] >> lane) & 1ull)
+        sh.list[nb + before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u))] = vals[j];
+      nb += total;
+    }
+    __syncthreads();
+  }
+  const int lo = (int)((int64_t)nb * sp / splits), hi = (int)((int64_t)nb * (sp + 1) / splits);
+
+  // Query fragments (the group's heads are the 16 MFMA columns, padded).
+  bf16x8 qb[4];
+  {
+    const bool hv = c16 < a.G;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = zero16();
+      if (hv) v = ldg16(a.q + (row * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
+      qb[ks] = as_bf16x8(v);
+    }
+  }
+  floatx4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float m = -1e30f, l = 0.f;
+  const uint16_t* vbase = a.vt + ((int64_t)g * kHeadDim * a.batch + s) * a.vt_ld;
+  const int64_t vdim = (int64_t)a.batch * a.vt_ld;
+
+  for (int r = lo + wave; r < hi; r += kSplitWaves) {
+    const int b = dense ? r : sh.list[r];
+    bf16x8 kf[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      int64_t krow = (int64_t)rk.start + kBlock * b + key_of(kt, c16);
+      krow = krow < a.rows_k ? krow : a.rows_k - 1;
+      const uint16_t* kp = a.k + (krow * a.h_kv + g) * kHeadDim + 8 * q4;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) kf[kt][ks] = as_bf16x8(ldg16(kp + 32 * ks));
+    }
+    u32x4 vb[8][2];
+    const uint16_t* vp = vbase + (int64_t)c16 * vdim + kBlock * b + 8 * q4;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) vb[dt][kk] = ldg16(vp + (int64_t)(16 * dt) * vdim + 32 * kk);
+    floatx4 sacc[4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) {
+      sacc[kt] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sacc[kt] = mfma16(kf[kt][ks], qb[ks], sacc[kt]);
+    }
+    // Online softmax update (keys after the query masked in its own block).
+    float v[4][4], mx = -__builtin_inff();
+    const int lim = t - kBlock * b - 8 * q4;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        v[kt][rr] = (b < bt || 32 * (kt >> 1) + 4 * (kt & 1) + rr <= lim) ? sacc[kt][rr] : -__builtin_inff();
+        mx = fmaxf(mx, v[kt][rr]);
+      }
+    mx = max_x32(max_x16(mx));
+    if (__ballot(mx * a.c > m * a.c + kLazyLog2) != 0) {
+      const float mn = fmaxf(m, mx);
+      const float alpha = fast_exp2((m - mn) * a.c);
+      m = mn;
+      l *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) o[dt][rr] *= alpha;
+    }
+    const float mc = m * a.c;
+    float p[4][4];
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        p[kt][rr] = fast_exp2(fmaf(v[kt][rr], a.c, -mc));
+        l += p[kt][rr];
+      }
+    bf16x8 pb[2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 w;
+      w[0] = pack_bf16x2(p[2 * kk][0], p[2 * kk][1]);
+      w[1] = pack_bf16x2(p[2 * kk][2], p[2 * kk][3]);
+      w[2] = pack_bf16x2(p[2 * kk + 1][0], p[2 * kk + 1][1]);
+      w[3] = pack_bf16x2(p[2 * kk + 1][2], p[2 * kk + 1][3]);
+      pb[kk] = as_bf16x8(w);
+    }
+    const bool partial = kBlock * b + kBlock > rk.len;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const u32x4 vv = partial ? clip_keys(vb[dt][kk], kBlock * b + 32 * kk + 8 * q4, rk.len) : vb[dt][kk];
+        o[dt] = mfma16(as_bf16x8(vv), pb[kk], o[dt]);
+      }
+  }
+
+  // Merge the four waves' states, then write the workgroup's partial.
+  const float lt = sum_x16(sum_x32(l));
+  if (q4 == 0) {
+    sh.pm[wave][c16] = m;
+    sh.pl[wave][c16] = lt;
+  }
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+    *reinterpret_cast<floatx4*>(&sh.po[wave][c16 * kHeadDim + 16 * dt + 4 * q4]) = o[dt];
+  __syncthreads();
+  const int h = tid >> 4, d0 = 8 * (tid & 15);
+  float M = sh.pm[0][h];
+#pragma unroll
+  for (int w = 1; w < kSplitWaves; ++w) M = fmaxf(M, sh.pm[w][h]);
+  float L = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll
+  for (int w = 0; w < kSplitWaves; ++w) {
+    const float wt = fast_exp2((sh.pm[w][h] - M) * a.c);
+    L += wt * sh.pl[w][h];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] += wt * sh.po[w][h * kHeadDim + d0 + i];
+  }
+  float* dst = part + (((int64_t)row * a.h_kv + g) * splits + sp) * kPartFloats;
+#pragma unroll
+  for (int i = 0; i < 8; i += 4)
+    *reinterpret_cast<floatx4*>(dst + h * kHeadDim + d0 + i) = floatx4{acc[i], acc[i + 1], acc[i + 2], acc[i + 3]};
+  if ((tid & 15) == 0) {
+    dst[16 * kHeadDim + h] = L;
+    dst[16 * kHeadDim + 16 + h] = M;
+  }
+}
+
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int splits, const float* part) {
+  const int g = blockIdx.x;
+  const int64_t row = blockIdx.y;
+  if (seq_of_row(a, row) < 0) return;
+  const int tid = threadIdx.x, h = tid >> 4, d0 = 8 * (tid & 15);
+  const float* src = part + ((int64_t)row * a.h_kv + g) * splits * kPartFloats;
+  float M = -__builtin_inff();
+  for (int p = 0; p < splits; ++p) M = fmaxf(M, src[p * kPartFloats + 16 * kHeadDim + 16 + h]);
+  float L = 0.f, acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  for (int p = 0; p < splits; ++p) {
+    const float* pp = src + p * kPartFloats;
+    const float wt = fast_exp2((pp[16 * kHeadDim + 16 + h] - M) * a.c);
+    L += wt * pp[16 * kHeadDim + h];
+    const floatx4 x0 = *reinterpret_cast<const floatx4*>(pp + h * kHeadDim + d0);
+    const floatx4 x1 = *reinterpret_cast<const floatx4*>(pp + h * kHeadDim + d0 + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[i] += wt * x0[i];
+      acc[4 + i] += wt * x1[i];
+    }
+  }
+  if (h >= a.G) return;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* dst = a.out + (row * a.h_q + g * a.G + h) * kHeadDim + d0;
+  u32x4 w;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
+  stg16(dst, w);
+  if (a.lse && (tid & 15) == 0)
+    a.lse[(int64_t)(g * a.G + h) * a.rows_q + row] = L > 0.f ? M * a.scale + logf(L) : -__builtin_inff();
+}
+
+}  // namespace
+
+hipError_t launch_attention_split(const AttnArgs& a, int64_t rows_q, int splits, float* part,
+                                  hipStream_t st) {
+  hipLaunchKernelGGL(attn_split_kernel, dim3(splits, a.h_kv, (unsigned)rows_q), dim3(kSplitThreads), 0, st, a,
+                     splits, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(a.h_kv, (unsigned)rows_q), dim3(256), 0, st, a, splits,
+                     (const float*)part);
+  return hipGetLastError();
+}
+
+}  // namespace infllmv2

@@ -86,4 +86,13 @@ hipError_t launch_topk(const TopkArgs& a, int batch, int h_kv, int max_seqlen_q,
                        hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st);
 
+// Split-K attention for launches with few query tiles (decode): every query
+// row's block set is split into `splits` ranges processed by separate
+// workgroups, each writing a partial (max, sums, unnormalised output) to
+// `part`; a second kernel merges the partials into out / lse.
+constexpr int kSplitMaxSel = 1024;                    // list entries per row on this path
+constexpr int kPartFloats = 16 * kHeadDim + 16 + 16;   // O[16][128], l[16], m[16] per head
+hipError_t launch_attention_split(const AttnArgs& a, int64_t rows_q, int splits, float* part,
+                                  hipStream_t st);
+
 }  // namespace infllmv2

@@ -87,7 +87,8 @@ class SparsePlan:
         self.block_idx = torch.empty((h_kv, rows_q, cfg.n_sel), dtype=torch.int32, device=device)
         ws1 = B.select_blocks_workspace(rows_q, h_q, h_kv, self.max_q, self.max_k, cfg.n_init,
                                         cfg.n_local, cfg.n_topk, self.approx)
-        ws2 = B.attn_workspace(h_kv, self.batch, self.max_q, self.max_k)
+        ws2 = B.attn_workspace(h_q, h_kv, self.batch, self.max_q, self.max_k, rows_q,
+                               n_sel=cfg.n_sel, n_init=cfg.n_init, n_local=cfg.n_local)
         self.ws_select = torch.empty(ws1, dtype=torch.uint8, device=device)
         self.ws_attn = torch.empty(max(1, ws2), dtype=torch.uint8, device=device)
 
@@ -123,7 +124,7 @@ class SparsePlan:
 class DensePlan:
     """Dense causal attention for the given sequences."""
 
-    def __init__(self, q_starts, q_lens, k_starts, k_lens, h_kv, cfg: SparseConfig,
+    def __init__(self, q_starts, q_lens, k_starts, k_lens, rows_q, h_q, h_kv, cfg: SparseConfig,
                  device="cuda", d=128):
         self.cfg, self.d = cfg, d
         self.batch = len(q_lens)
@@ -133,7 +134,7 @@ class DensePlan:
         self.used_q = _i32(q_lens, device)
         self.cu_k = _i32(k_starts, device)
         self.used_k = _i32(k_lens, device)
-        ws = B.attn_workspace(h_kv, self.batch, self.max_q, self.max_k)
+        ws = B.attn_workspace(h_q, h_kv, self.batch, self.max_q, self.max_k, rows_q)
         self.ws = torch.empty(max(1, ws), dtype=torch.uint8, device=device)
 
     def run(self, q, k, v, out, lse=None):
@@ -160,7 +161,7 @@ class SwitchPlan:
         dl = [seqlens[i] for i in self.dense_ids]
         ss = [starts[i] for i in self.sparse_ids]
         sl = [seqlens[i] for i in self.sparse_ids]
-        self.dense = DensePlan(ds, dl, ds, dl, h_kv, cfg, device, d)
+        self.dense = DensePlan(ds, dl, ds, dl, self.rows, h_q, h_kv, cfg, device, d)
         self.sparse = SparsePlan(ss, sl, ss, sl, self.rows, h_q, h_kv, cfg, device, d)
 
     def run(self, q, k, v, out, lse=None):
@@ -213,6 +214,9 @@ class DecodeState:
         ws = B.select_blocks_workspace(batch, h_q, h_kv, 1, cap, cfg.n_init, cfg.n_local,
                                        cfg.n_topk, self.approx)
         self.ws_select = torch.empty(ws, dtype=torch.uint8, device=device)
+        ws = B.attn_workspace(h_q, h_kv, batch, 1, cap, batch, v_seq_stride=cap, n_sel=cfg.n_sel,
+                              n_init=cfg.n_init, n_local=cfg.n_local)
+        self.ws_attn = torch.empty(max(1, ws), dtype=torch.uint8, device=device)
 
     def fill(self, k_rows, v_rows, lens):
         """Load prefix K/V (lists of [len, h_kv, d] bf16 tensors) and compress."""
@@ -265,4 +269,4 @@ class DecodeState:
                         c.n_topk, c.scale(self.d), self.block_idx, self.ws_select)
         B.sparse_attn(q_new, self.k_cache, self.vt_cache, self.cu_q, self.used_q, self.cu_k,
                       self.used_k, self.batch, 1, max_len, self.block_idx, c.n_init, c.n_local,
-                      c.scale(self.d), out, None, None, v_seq_stride=self.cap)
+                      c.scale(self.d), out, None, self.ws_attn, v_seq_stride=self.cap)
