@@ -127,10 +127,10 @@ def compress_k(k, cu_seqlens_k, seqused_k, batch, max_seqlen_k, kernel_size, str
 
 
 def select_blocks_workspace(rows_q, h_q, h_kv, max_seqlen_q, max_seqlen_k, n_init, n_local,
-                            n_topk, approx=False) -> int:
+                            n_topk, approx=False, batch=1) -> int:
     size = ctypes.c_size_t(0)
     _check(load().infllmv2_select_blocks(
-        None, None, _P(1) if approx else None, None, None, None, None, None, None, 1,
+        None, None, _P(1) if approx else None, None, None, None, None, None, None, batch,
         max_seqlen_q, max_seqlen_k, rows_q, 0, 0, h_q, h_kv, 128, 64, n_init, n_local, n_topk,
         32, 16, 128, 64, 5, 4, 1, 1.0, None, ctypes.byref(size), None, None))
     return size.value

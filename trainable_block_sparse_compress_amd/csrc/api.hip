@@ -53,16 +53,30 @@ constexpr int kMaxGrid = 65535;
 
 // Workspace of the scoring path: fp32 LSE [h_q, rows_q] + fp32 block scores
 // [h_kv, rows_q, bs_ld].
+// Launches with few query tiles (decode) split every row's compressed keys
+// over several workgroups; pass 1 then leaves (max, sum) partials instead of
+// the LSE.
 struct SelectLayout {
   int64_t bs_ld;
-  size_t lse_bytes, bs_bytes, total;
+  int splits;                 // 0: tile kernels
+  size_t lse_bytes, bs_bytes, part_bytes, total;
 };
-SelectLayout select_layout(int64_t rows_q, int h_q, int h_kv, int max_seqlen_k) {
+int select_splits(int64_t rows_q, int batch, int max_seqlen_q, int max_seqlen_k, int h_kv) {
+  const int64_t tiles = ceil_div(std::max(1, max_seqlen_q), 16) * h_kv * std::max(1, batch);
+  if (tiles >= 512 || max_seqlen_q > 64 || rows_q > kMaxGrid || rows_q < 1) return 0;
+  const int64_t want = ceil_div(512, rows_q * h_kv);
+  const int64_t cap = std::max<int64_t>(1, ceil_div(std::max(1, max_seqlen_k), 16) / 64);   // >= 64 keys each
+  return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, (int64_t)64}));
+}
+SelectLayout select_layout(int64_t rows_q, int batch, int max_seqlen_q, int h_q, int h_kv,
+                           int max_seqlen_k) {
   SelectLayout L;
   L.bs_ld = round_up(std::max<int64_t>(1, ceil_div(max_seqlen_k, kBlock)), 4);
+  L.splits = select_splits(rows_q, batch, max_seqlen_q, max_seqlen_k, h_kv);
   L.lse_bytes = align_up((size_t)h_q * (size_t)rows_q * sizeof(float));
   L.bs_bytes = align_up((size_t)h_kv * (size_t)rows_q * (size_t)L.bs_ld * sizeof(float));
-  L.total = L.lse_bytes + L.bs_bytes;
+  L.part_bytes = L.splits > 0 ? align_up((size_t)rows_q * h_kv * L.splits * 32 * sizeof(float)) : 0;
+  L.total = L.lse_bytes + L.bs_bytes + L.part_bytes;
   return L;
 }
 
@@ -299,7 +313,7 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   REQUIRE(std::isfinite(softmax_scale) && softmax_scale > 0.f, INFLLMV2_EINVAL, "softmax_scale must be finite and > 0");
   REQUIRE(ceil_div(max_seqlen_k, kBlock) <= kMaxBlocks, INFLLMV2_EUNSUPPORTED,
           "more than %d blocks per sequence", kMaxBlocks);
-  const SelectLayout L = select_layout(rows_q, h_q, h_kv, max_seqlen_k);
+  const SelectLayout L = select_layout(rows_q, batch, max_seqlen_q, h_q, h_kv, max_seqlen_k);
   bool query = false;
   rc = workspace_check(workspace, workspace_bytes, L.total, &query);
   if (rc || query) return rc;
@@ -329,6 +343,9 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   sa.lse = reinterpret_cast<float*>(ws);
   sa.bs = reinterpret_cast<float*>(ws + L.lse_bytes);
   sa.bs_ld = L.bs_ld;
+  sa.batch = batch;
+  sa.splits = L.splits;
+  sa.part = L.splits > 0 ? reinterpret_cast<float*>(ws + L.lse_bytes + L.bs_bytes) : nullptr;
 
   // Pass 1: exact LSE over the stage-1 keys, or the approximation over the
   // coarse keys.
@@ -338,7 +355,8 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   p1.c_rows = approx ? c2_rows : c1_rows;
   p1.win_kernel = approx ? c2_kernel : c1_kernel;
   p1.win_stride = approx ? c2_stride : c1_stride;
-  rc = hip_status(launch_score_lse(p1, batch, max_seqlen_q, st), "score_lse launch");
+  rc = hip_status(L.splits > 0 ? launch_score_lse_split(p1, st) : launch_score_lse(p1, batch, max_seqlen_q, st),
+                  "score_lse launch");
   if (rc) return rc;
 
   // Pass 2: probabilities, group sum and max pool -> block scores.
@@ -348,7 +366,9 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   p2.c_rows = c1_rows;
   p2.win_kernel = c1_kernel;
   p2.win_stride = c1_stride;
-  rc = hip_status(launch_score_blocks(p2, batch, max_seqlen_q, st), "score_blocks launch");
+  rc = hip_status(L.splits > 0 ? launch_score_blocks_split(p2, st)
+                                : launch_score_blocks(p2, batch, max_seqlen_q, st),
+                  "score_blocks launch");
   if (rc) return rc;
 
   TopkArgs ta;

@@ -46,6 +46,9 @@ struct ScoreArgs {
   float* lse;               // [h_q, rows_q], natural log
   float* bs;                // [h_kv, rows_q, bs_ld] block scores
   int64_t bs_ld;
+  int batch;                // split path: sequences (row -> sequence search)
+  int splits;               // split path: window ranges per (row, KV group)
+  float* part;              // split path: LSE partials [rows_q, h_kv, splits, 16, 2]
 };
 
 struct TopkArgs {
@@ -82,6 +85,11 @@ hipError_t launch_compress(const CompressArgs& a, int batch, int max_windows, hi
 hipError_t launch_transpose_v(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_score_lse(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st);
 hipError_t launch_score_blocks(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st);
+// Split-K scoring for launches with few query tiles (decode): pass 1 writes
+// per-range (max, sum) partials of the LSE, pass 2 merges them and writes the
+// block scores of its range.
+hipError_t launch_score_lse_split(const ScoreArgs& a, hipStream_t st);
+hipError_t launch_score_blocks_split(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, int batch, int h_kv, int max_seqlen_q, int max_blocks,
                        hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st);

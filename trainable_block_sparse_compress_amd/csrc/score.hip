@@ -381,3 +381,219 @@ hipError_t launch_score_blocks(const ScoreArgs& a, int batch, int max_seqlen_q, 
 }
 
 }  // namespace infllmv2
+
+// ---------------------------------------------------------------------------
+// Split-K scoring.  With few query tiles (decode) a workgroup takes one query
+// row, one KV group and one range of compressed keys; its waves work on
+// chunks of 16 keys loaded straight into registers (the 16 heads of the group
+// are the MFMA rows, 16 keys the columns).  Pass 1 keeps an exact running
+// max per lane and head and writes one (max, sum) partial per range; pass 2
+// merges a row's partials into its LSE and writes the block scores of its
+// range, each wave walking a contiguous run of chunks so that the window
+// before every quad (4b - 1) is at hand.
+// ---------------------------------------------------------------------------
+namespace infllmv2 {
+namespace {
+
+constexpr int kSplitScoreWaves = 4;
+
+__device__ __forceinline__ int seq_of_row_s(const ScoreArgs& a, int64_t row) {
+  int lo = 0, hi = a.batch - 1;
+  if (hi < 0) return -1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_q[mid] <= row) lo = mid;
+    else hi = mid - 1;
+  }
+  const SeqRange r = seq_range(a.cu_q, a.used_q, lo);
+  return (row >= r.start && row < (int64_t)r.start + r.len) ? lo : -1;
+}
+
+// Row setup shared by both passes; false when the row needs no scores.
+struct SplitRow {
+  int s, t, bt, nv;
+  int64_t c0;
+};
+__device__ __forceinline__ bool split_row(const ScoreArgs& a, int64_t row, SplitRow& r) {
+  r.s = seq_of_row_s(a, row);
+  if (r.s < 0) return false;
+  const SeqRange rq = seq_range(a.cu_q, a.used_q, r.s);
+  const SeqRange rk = seq_range(a.cu_k, a.used_k, r.s);
+  r.t = rk.len - rq.len + (int)(row - rq.start);
+  if (r.t < 0) return false;
+  r.bt = r.t / kBlock;
+  if (r.bt - a.n_local - a.n_init + 1 <= a.n_topk) return false;   // keeps every candidate
+  const int nwin = rk.len >= a.win_kernel ? (rk.len - a.win_kernel) / a.win_stride + 1 : 0;
+  r.nv = n_visible(r.t, a.win_kernel, a.win_stride, nwin);
+  r.c0 = a.cu_c[r.s];
+  return true;
+}
+
+// S^T chunk: heads (rows) x 16 keys j0 .. j0+15 (columns) of one query row.
+__device__ __forceinline__ floatx4 split_chunk(const ScoreArgs& a, const bf16x8 (&qa)[4], int g, int64_t c0,
+                                               int j0, int c16, int q4) {
+  int64_t rowc = c0 + j0 + c16;
+  rowc = rowc < a.c_rows ? rowc : a.c_rows - 1;
+  const uint16_t* kp = a.kc + ((int64_t)g * a.c_rows + rowc) * kHeadDim + 8 * q4;
+  bf16x8 b[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) b[ks] = as_bf16x8(ldg16(kp + 32 * ks));
+  floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) acc = mfma16(qa[ks], b[ks], acc);
+  return acc;
+}
+
+__device__ __forceinline__ void load_q(const ScoreArgs& a, int64_t row, int g, int c16, int q4, bf16x8 (&qa)[4]) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    u32x4 v = zero16();
+    if (c16 < a.G) v = ldg16(a.q + (row * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
+    qa[ks] = as_bf16x8(v);
+  }
+}
+
+__global__ __launch_bounds__(64 * kSplitScoreWaves) void score_lse_split_kernel(ScoreArgs a) {
+  __shared__ float red[kSplitScoreWaves][16][2];
+  const int sp = blockIdx.x, g = blockIdx.y;
+  const int64_t row = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
+  const int wave = tid >> 6;
+  SplitRow r;
+  if (!split_row(a, row, r)) return;
+  bf16x8 qa[4];
+  load_q(a, row, g, c16, q4, qa);
+  const int nch = (r.nv + 15) >> 4;
+  const int ca = (int)((int64_t)nch * sp / a.splits), cb = (int)((int64_t)nch * (sp + 1) / a.splits);
+  float m[4], sm[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    m[i] = -__builtin_inff();
+    sm[i] = 0.f;
+  }
+  for (int ch = ca + wave; ch < cb; ch += kSplitScoreWaves) {
+    const floatx4 acc = split_chunk(a, qa, g, r.c0, 16 * ch, c16, q4);
+    const bool ok = 16 * ch + c16 < r.nv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (ok) {
+        const float mn = fmaxf(m[i], acc[i]);
+        sm[i] = sm[i] * fast_exp2((m[i] - mn) * a.c) + fast_exp2((acc[i] - mn) * a.c);
+        m[i] = mn;
+      }
+    }
+  }
+  // Combine the 16 lanes (keys) of each row group, then the waves.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float mm = m[i], ss = sm[i];
+#pragma unroll
+    for (int step = 0; step < 4; ++step) {
+      float m2, s2;
+      if (step == 0) { m2 = dpp_f32<0xB1>(mm, mm); s2 = dpp_f32<0xB1>(ss, ss); }        // quad_perm 1,0,3,2
+      else if (step == 1) { m2 = dpp_f32<0x4E>(mm, mm); s2 = dpp_f32<0x4E>(ss, ss); }   // quad_perm 2,3,0,1
+      else if (step == 2) { m2 = dpp_f32<0x124>(mm, mm); s2 = dpp_f32<0x124>(ss, ss); } // row_ror:4
+      else { m2 = dpp_f32<0x128>(mm, mm); s2 = dpp_f32<0x128>(ss, ss); }                // row_ror:8
+      const float mn = fmaxf(mm, m2);
+      ss = (mm > -__builtin_inff() ? ss * fast_exp2((mm - mn) * a.c) : 0.f) +
+           (m2 > -__builtin_inff() ? s2 * fast_exp2((m2 - mn) * a.c) : 0.f);
+      mm = mn;
+    }
+    if (c16 == 0) {
+      red[wave][4 * q4 + i][0] = mm;
+      red[wave][4 * q4 + i][1] = ss;
+    }
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float mm = red[0][tid][0], ss = red[0][tid][1];
+#pragma unroll
+    for (int w = 1; w < kSplitScoreWaves; ++w) {
+      const float m2 = red[w][tid][0], s2 = red[w][tid][1];
+      const float mn = fmaxf(mm, m2);
+      ss = (mm > -__builtin_inff() ? ss * fast_exp2((mm - mn) * a.c) : 0.f) +
+           (m2 > -__builtin_inff() ? s2 * fast_exp2((m2 - mn) * a.c) : 0.f);
+      mm = mn;
+    }
+    float* dst = a.part + (((int64_t)row * a.h_kv + g) * a.splits + sp) * 32;
+    dst[2 * tid] = mm;
+    dst[2 * tid + 1] = ss;
+  }
+}
+
+__global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_split_kernel(ScoreArgs a) {
+  const int sp = blockIdx.x, g = blockIdx.y;
+  const int64_t row = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
+  const int wave = tid >> 6;
+  SplitRow r;
+  if (!split_row(a, row, r)) return;
+  // LSE of the lane's four heads (in log2 units, scaled) from the partials.
+  float Lc[4];
+  {
+    const float* src = a.part + ((int64_t)row * a.h_kv + g) * a.splits * 32;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int h = 4 * q4 + i;
+      float mm = -__builtin_inff();
+      for (int p = 0; p < a.splits; ++p) mm = fmaxf(mm, src[p * 32 + 2 * h]);
+      float ss = 0.f;
+      for (int p = 0; p < a.splits; ++p) {
+        const float m2 = src[p * 32 + 2 * h];
+        if (m2 > -__builtin_inff()) ss += src[p * 32 + 2 * h + 1] * fast_exp2((m2 - mm) * a.c);
+      }
+      Lc[i] = ss > 0.f ? mm * a.c + __builtin_amdgcn_logf(ss) : __builtin_inff();
+    }
+  }
+  bf16x8 qa[4];
+  load_q(a, row, g, c16, q4, qa);
+  // Windows overlapping candidate blocks n_init .. bt - n_local: chunks of 16.
+  const int b_hi = r.bt - a.n_local;
+  const int cfirst = max(0, 4 * a.n_init - 1) >> 4;
+  const int clast = (4 * b_hi + 3) >> 4;   // inclusive
+  const int nch = clast - cfirst + 1;
+  const int ca0 = cfirst + (int)((int64_t)nch * sp / a.splits);
+  const int cb0 = cfirst + (int)((int64_t)nch * (sp + 1) / a.splits);
+  const int ca = ca0 + (int)((int64_t)(cb0 - ca0) * wave / kSplitScoreWaves);
+  const int cb = ca0 + (int)((int64_t)(cb0 - ca0) * (wave + 1) / kSplitScoreWaves);
+  if (ca >= cb) return;
+  auto chunk_sum = [&](int ch) -> float {
+    const floatx4 acc = split_chunk(a, qa, g, r.c0, 16 * ch, c16, q4);
+    float sum = fast_exp2(fmaf(acc[0], a.c, -Lc[0]));
+#pragma unroll
+    for (int i = 1; i < 4; ++i) sum += fast_exp2(fmaf(acc[i], a.c, -Lc[i]));
+    sum = sum_x16(sum_x32(sum));   // all heads of the group: lane c16 -> key 16 ch + c16
+    return 16 * ch + c16 < r.nv ? sum : 0.f;
+  };
+  // Window 16 ca - 1 (the last of the previous chunk) feeds the first quad.
+  float carry = 0.f;
+  if (ca > 0) carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(chunk_sum(ca - 1)), 15));
+  float* bsr = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld;
+  for (int ch = ca; ch < cb; ++ch) {
+    const float S = chunk_sum(ch);
+    const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));       // quad_perm 1,0,3,2
+    const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));    // quad_perm 2,3,0,1
+    const float prev = dpp_f32<0x138>(carry, S);          // wave_shr:1
+    carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 15));
+    if (lane < 16 && (lane & 3) == 0) {
+      const int b = 4 * ch + (lane >> 2);
+      if (b >= a.n_init && b <= b_hi && b < a.bs_ld) bsr[b] = fmaxf(qm, prev);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score_lse_split(const ScoreArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(score_lse_split_kernel, dim3(a.splits, a.h_kv, (unsigned)a.rows_q),
+                     dim3(64 * kSplitScoreWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_score_blocks_split(const ScoreArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(score_blocks_split_kernel, dim3(a.splits, a.h_kv, (unsigned)a.rows_q),
+                     dim3(64 * kSplitScoreWaves), 0, st, a);
+  return hipGetLastError();
+}
+
+}  // namespace infllmv2

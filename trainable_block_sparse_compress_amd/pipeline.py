@@ -86,7 +86,7 @@ class SparsePlan:
             self.cu_c2, self.kc2 = None, None
         self.block_idx = torch.empty((h_kv, rows_q, cfg.n_sel), dtype=torch.int32, device=device)
         ws1 = B.select_blocks_workspace(rows_q, h_q, h_kv, self.max_q, self.max_k, cfg.n_init,
-                                        cfg.n_local, cfg.n_topk, self.approx)
+                                        cfg.n_local, cfg.n_topk, self.approx, batch=self.batch)
         ws2 = B.attn_workspace(h_q, h_kv, self.batch, self.max_q, self.max_k, rows_q,
                                n_sel=cfg.n_sel, n_init=cfg.n_init, n_local=cfg.n_local)
         self.ws_select = torch.empty(ws1, dtype=torch.uint8, device=device)
@@ -212,7 +212,7 @@ class DecodeState:
         self.begin2 = torch.zeros(batch, dtype=torch.int32, device=device)
         self.block_idx = torch.empty((h_kv, batch, cfg.n_sel), dtype=torch.int32, device=device)
         ws = B.select_blocks_workspace(batch, h_q, h_kv, 1, cap, cfg.n_init, cfg.n_local,
-                                       cfg.n_topk, self.approx)
+                                       cfg.n_topk, self.approx, batch=batch)
         self.ws_select = torch.empty(ws, dtype=torch.uint8, device=device)
         ws = B.attn_workspace(h_q, h_kv, batch, 1, cap, batch, v_seq_stride=cap, n_sel=cfg.n_sel,
                               n_init=cfg.n_init, n_local=cfg.n_local)
