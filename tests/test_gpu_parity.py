@@ -447,15 +447,49 @@ def test_varlen_switch(lib):
                 assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, ("sparse", s, t, ma)
 
 
-def test_decode_steps(lib):
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_split_select_short_queries(lib, mode):
+    """Few query tiles (5, 1 and 3 queries at the end of 6000, 9001 and 4500
+    keys) take the split-K scoring kernels; every row's selection is checked
+    against the oracle's."""
+    say(f"split select {mode}")
+    h_q, h_kv = 32, 2
+    klens, qlens = [6000, 9001, 4500], [5, 1, 3]
+    p = R.Params(lse_mode=mode)
+    pr = p.with_(round_kc=True)
+    inp = D.make_prefill(33, klens, h_q, h_kv, n_needles=4)
+    kst = _starts(klens)
+    qrows = [kst[s] + klens[s] - qlens[s] + i for s in range(3) for i in range(qlens[s])]
+    qst = _starts(qlens)
+    plan = P.SparsePlan(qst, qlens, kst, klens, len(qrows), h_q, h_kv, _cfg(p))
+    plan.compress(to_dev(inp.k))
+    plan.select(to_dev(np.ascontiguousarray(inp.q[qrows])))
+    torch.cuda.synchronize()
+    idx = plan.block_idx.cpu().numpy()
+    for s in range(3):
+        Ks = inp.k[kst[s]:kst[s] + klens[s]]
+        KC1 = R.compress_keys(Ks, 32, 16, True)
+        KC2 = R.compress_keys(Ks, 128, 64, True) if mode == "approx" else None
+        for i in range(qlens[s]):
+            t = klens[s] - qlens[s] + i
+            sel, diag = R.select_token(inp.q[kst[s] + t], t, KC1, KC2, h_q // h_kv, pr)
+            for g in range(h_kv):
+                gl = [int(b) for b in idx[g, qst[s] + i] if b >= 0]
+                ok, _, _ = check_selection(gl, sel[g], diag["info"][g], t, pr)
+                assert ok, (s, i, g)
+
+
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_decode_steps(lib, mode):
     """Decode: incremental compression, selection for one new token per
     sequence and sparse attention over a transposed V cache, checked at
-    every step against the oracle's row for that position."""
-    say("decode steps")
+    every step against the oracle's row for that position (split-K scoring
+    and attention)."""
+    say(f"decode steps {mode}")
     batch, h_q, h_kv, steps = 3, 32, 2, 6
     lens0 = [7000, 9001, 6400]
     cap = 9088
-    p = R.Params()
+    p = R.Params(lse_mode=mode)
     pr = p.with_(round_kc=True)
     inp = D.make_prefill(4, [cap] * batch, h_q, h_kv, n_needles=4)
     st = _starts([cap] * batch)
@@ -481,7 +515,8 @@ def test_decode_steps(lib):
             t = pos[s]
             Ks = inp.k[st[s]:st[s] + t + 1]
             KC1 = R.compress_keys(Ks, 32, 16, True)
-            sel, diag = R.select_token(inp.q[st[s] + t], t, KC1, None, 16, pr)
+            KC2 = R.compress_keys(Ks, 128, 64, True) if mode == "approx" else None
+            sel, diag = R.select_token(inp.q[st[s] + t], t, KC1, KC2, 16, pr)
             gl = [[int(b) for b in idx[g, s] if b >= 0] for g in range(h_kv)]
             for g in range(h_kv):
                 ok, _, _ = check_selection(gl[g], sel[g], diag["info"][g], t, pr)
