@@ -89,7 +89,6 @@ size_t vt_bytes(int h_kv, int batch, int max_seqlen_k) {
 // Launches with fewer query tiles than this take the split-K path.
 constexpr int64_t kSplitTileLimit = 512;
 constexpr int kSplitTargetWgs = 512;
-constexpr int kSplitMaxSplits = 64;
 
 // Split count of the split-K attention path, or 0 for the tile kernel.
 int attn_splits(int64_t rows_q, int batch, int max_seqlen_q, int max_seqlen_k, int h_kv, bool dense,
@@ -97,6 +96,7 @@ int attn_splits(int64_t rows_q, int batch, int max_seqlen_q, int max_seqlen_k, i
   const int64_t tiles = ceil_div(std::max(1, max_seqlen_q), 16) * h_kv * std::max(1, batch);
   if (tiles >= kSplitTileLimit || max_seqlen_q > 64 || rows_q > kMaxGrid || rows_q < 1) return 0;
   if (!dense && (int64_t)n_sel + n_init + n_local > kSplitMaxSel) return 0;
+  if (ceil_div(std::max(1, max_seqlen_k), kBlock) > 65536) return 0;   // block bitmap of the split path
   const int64_t blocks = dense ? ceil_div(std::max(1, max_seqlen_k), kBlock)
                                : std::min<int64_t>((int64_t)n_sel + n_init + n_local,
                                                    ceil_div(std::max(1, max_seqlen_k), kBlock));
@@ -383,7 +383,9 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   ta.n_local = n_local;
   ta.n_topk = n_topk;
   ta.idx = block_idx;
-  rc = hip_status(launch_topk(ta, batch, h_kv, max_seqlen_q, (int)ceil_div(max_seqlen_k, kBlock), st),
+  ta.batch = batch;
+  rc = hip_status(L.splits > 0 ? launch_topk_rows(ta, h_kv, (int)ceil_div(max_seqlen_k, kBlock), st)
+                               : launch_topk(ta, batch, h_kv, max_seqlen_q, (int)ceil_div(max_seqlen_k, kBlock), st),
                   "topk launch");
   if (rc) return rc;
   return ok();

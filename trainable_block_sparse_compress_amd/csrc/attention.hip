@@ -630,9 +630,12 @@ namespace {
 constexpr int kSplitWaves = 4;
 constexpr int kSplitThreads = 64 * kSplitWaves;
 
+constexpr int kWordsPerThread = 8;   // bitmap of up to 65536 blocks (4M keys)
+
 struct SplitLds {
+  uint32_t bits[kWordsPerThread * kSplitThreads];
   int32_t list[kSplitMaxSel];
-  int32_t cnt[kSplitMaxSel / kSplitThreads][kSplitWaves];
+  int32_t cnt[kSplitWaves];
   float pm[kSplitWaves][16];   // running max per head (the lanes of a head share it)
   float pl[kSplitWaves][16];
   float po[kSplitWaves][16 * kHeadDim];
@@ -672,60 +675,55 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
   if (dense) {
     nb = min(bt + 1, nvt);
   } else {
-    // Candidates: the list, then the init blocks, then the local blocks.
-    const int n_cand = a.n_sel + a.n_init + a.n_local;
-    int p2 = 1;
-    while (p2 < n_cand) p2 <<= 1;
+    // Set of candidate blocks (the list, the init blocks, the local blocks)
+    // as a bitmap over blocks 0..bt, then listed ascending.
+    const int nbits = min(min(bt + 1, nvt), kWordsPerThread * kSplitThreads * 32);
+    const int nwords = (nbits + 31) >> 5;
+    for (int w = tid; w < nwords; w += kSplitThreads) sh.bits[w] = 0u;
+    __syncthreads();
     const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + row) * a.n_sel;
-    for (int i = tid; i < p2; i += kSplitThreads) {
-      int b = -1;
+    const int n_cand = a.n_sel + a.n_init + a.n_local;
+    for (int i = tid; i < n_cand; i += kSplitThreads) {
+      int b;
       if (i < a.n_sel) b = list[i];
       else if (i < a.n_sel + a.n_init) b = i - a.n_sel;
-      else if (i < n_cand) b = bt - (i - a.n_sel - a.n_init);
-      sh.list[i] = (b >= 0 && b <= bt && b < nvt) ? b : 0x7fffffff;
+      else b = bt - (i - a.n_sel - a.n_init);
+      if (b >= 0 && b < nbits) atomicOr(&sh.bits[b >> 5], 1u << (b & 31));
     }
     __syncthreads();
-    for (int k = 2; k <= p2; k <<= 1) {          // bitonic sort
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < p2; i += kSplitThreads) {
-          const int pi = i ^ j;
-          if (pi > i) {
-            const int x = sh.list[i], y = sh.list[pi];
-            if (((i & k) == 0) == (x > y)) {
-              sh.list[i] = y;
-              sh.list[pi] = x;
-            }
-          }
-        }
-        __syncthreads();
-      }
-    }
-    int vals[kSplitMaxSel / kSplitThreads];
-    uint64_t bal[kSplitMaxSel / kSplitThreads];
+    // Thread tid owns words kWordsPerThread*tid .. +kWordsPerThread-1.
+    uint32_t wv[kWordsPerThread];
+    int cnt = 0;
 #pragma unroll
-    for (int j = 0; j < kSplitMaxSel / kSplitThreads; ++j) {
-      const int i = kSplitThreads * j + tid;
-      const int v = i < p2 ? sh.list[i] : 0x7fffffff;
-      const bool keep = v != 0x7fffffff && (i == 0 || sh.list[i - 1] != v);
-      vals[j] = v;
-      bal[j] = __ballot(keep);
-      if (lane == 0) sh.cnt[j][wave] = __builtin_popcountll(bal[j]);
+    for (int j = 0; j < kWordsPerThread; ++j) {
+      const int w = kWordsPerThread * tid + j;
+      wv[j] = w < nwords ? sh.bits[w] : 0u;
+      cnt += __builtin_popcount(wv[j]);
     }
+    int incl = cnt;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) sh.cnt[wave] = incl;
     __syncthreads();
+    int base = 0;
     nb = 0;
 #pragma unroll
-    for (int j = 0; j < kSplitMaxSel / kSplitThreads; ++j) {
-      int before = 0, total = 0;
+    for (int w = 0; w < kSplitWaves; ++w) {
+      base += w < wave ? sh.cnt[w] : 0;
+      nb += sh.cnt[w];
+    }
+    int pos = base + incl - cnt;
 #pragma unroll
-      for (int w = 0; w < kSplitWaves; ++w) {
-        const int c = sh.cnt[j][w];
-        before += w < wave ? c : 0;
-        total += c;
+    for (int j = 0; j < kWordsPerThread; ++j) {
+      uint32_t x = wv[j];
+      while (x) {
+        const int bit = __builtin_ctz(x);
+        x &= x - 1u;
+        sh.list[pos++] = 32 * (kWordsPerThread * tid + j) + bit;
       }
-      if ((bal[j] >> lane) & 1ull)
-        sh.list[nb + before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
-                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u))] = vals[j];
-      nb += total;
     }
     __syncthreads();
   }
@@ -858,29 +856,50 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 }
 
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int splits, const float* part) {
+  __shared__ float wt[kSplitMaxSplits][16];
+  __shared__ float lp[kSplitMaxSplits][16];
+  __shared__ float Mh[16], Lh[16];
   const int g = blockIdx.x;
   const int64_t row = blockIdx.y;
   if (seq_of_row(a, row) < 0) return;
   const int tid = threadIdx.x, h = tid >> 4, d0 = 8 * (tid & 15);
   const float* src = part + ((int64_t)row * a.h_kv + g) * splits * kPartFloats;
-  float M = -__builtin_inff();
-  for (int p = 0; p < splits; ++p) M = fmaxf(M, src[p * kPartFloats + 16 * kHeadDim + 16 + h]);
-  float L = 0.f, acc[8];
+  // Per-split maxima of every head, then each head's weights and sum.
+  for (int i = tid; i < 16 * splits; i += 256) {
+    wt[i >> 4][i & 15] = src[(i >> 4) * kPartFloats + 16 * kHeadDim + 16 + (i & 15)];
+    lp[i >> 4][i & 15] = src[(i >> 4) * kPartFloats + 16 * kHeadDim + (i & 15)];
+  }
+  __syncthreads();
+  if (tid < 16) {
+    float M = -__builtin_inff();
+    for (int p = 0; p < splits; ++p) M = fmaxf(M, wt[p][tid]);
+    float L = 0.f;
+    for (int p = 0; p < splits; ++p) {
+      const float w = fast_exp2((wt[p][tid] - M) * a.c);
+      wt[p][tid] = w;
+      L += w * lp[p][tid];
+    }
+    Mh[tid] = M;
+    Lh[tid] = L;
+  }
+  __syncthreads();
+  float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+#pragma unroll 4
   for (int p = 0; p < splits; ++p) {
-    const float* pp = src + p * kPartFloats;
-    const float wt = fast_exp2((pp[16 * kHeadDim + 16 + h] - M) * a.c);
-    L += wt * pp[16 * kHeadDim + h];
-    const floatx4 x0 = *reinterpret_cast<const floatx4*>(pp + h * kHeadDim + d0);
-    const floatx4 x1 = *reinterpret_cast<const floatx4*>(pp + h * kHeadDim + d0 + 4);
+    const float* pp = src + p * kPartFloats + h * kHeadDim + d0;
+    const floatx4 x0 = *reinterpret_cast<const floatx4*>(pp);
+    const floatx4 x1 = *reinterpret_cast<const floatx4*>(pp + 4);
+    const float w = wt[p][h];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      acc[i] += wt * x0[i];
-      acc[4 + i] += wt * x1[i];
+      acc[i] += w * x0[i];
+      acc[4 + i] += w * x1[i];
     }
   }
   if (h >= a.G) return;
+  const float L = Lh[h];
   const float inv = L > 0.f ? 1.f / L : 0.f;
   uint16_t* dst = a.out + (row * a.h_q + g * a.G + h) * kHeadDim + d0;
   u32x4 w;
@@ -888,7 +907,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int splits,
   for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(acc[2 * i] * inv, acc[2 * i + 1] * inv);
   stg16(dst, w);
   if (a.lse && (tid & 15) == 0)
-    a.lse[(int64_t)(g * a.G + h) * a.rows_q + row] = L > 0.f ? M * a.scale + logf(L) : -__builtin_inff();
+    a.lse[(int64_t)(g * a.G + h) * a.rows_q + row] = L > 0.f ? Mh[h] * a.scale + logf(L) : -__builtin_inff();
 }
 
 }  // namespace

@@ -61,6 +61,7 @@ struct TopkArgs {
   int64_t rows_q;
   int n_init, n_local, n_topk;
   int32_t* idx;             // [h_kv, rows_q, n_sel]
+  int batch;                // row path: sequences (row -> sequence search)
 };
 
 struct AttnArgs {
@@ -92,6 +93,9 @@ hipError_t launch_score_lse_split(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_score_blocks_split(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, int batch, int h_kv, int max_seqlen_q, int max_blocks,
                        hipStream_t st);
+// Top-k with a whole workgroup per (query row, KV group), for launches with
+// few query rows (decode).
+hipError_t launch_topk_rows(const TopkArgs& a, int h_kv, int max_blocks, hipStream_t st);
 hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st);
 
 // Split-K attention for launches with few query tiles (decode): every query
@@ -99,6 +103,7 @@ hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st)
 // workgroups, each writing a partial (max, sums, unnormalised output) to
 // `part`; a second kernel merges the partials into out / lse.
 constexpr int kSplitMaxSel = 1024;                    // list entries per row on this path
+constexpr int kSplitMaxSplits = 64;                   // splits per (row, KV group)
 constexpr int kPartFloats = 16 * kHeadDim + 16 + 16;   // O[16][128], l[16], m[16] per head
 hipError_t launch_attention_split(const AttnArgs& a, int64_t rows_q, int splits, float* part,
                                   hipStream_t st);

@@ -429,15 +429,18 @@ __device__ __forceinline__ bool split_row(const ScoreArgs& a, int64_t row, Split
   return true;
 }
 
-// S^T chunk: heads (rows) x 16 keys j0 .. j0+15 (columns) of one query row.
-__device__ __forceinline__ floatx4 split_chunk(const ScoreArgs& a, const bf16x8 (&qa)[4], int g, int64_t c0,
-                                               int j0, int c16, int q4) {
+// Key fragments of the 16-key chunk j0 .. j0+15 (B operand: lane c16 holds
+// key j0 + c16, dims 32 ks + 8 q4 .. +8), rows clamped to the tensor.
+__device__ __forceinline__ void chunk_keys(const ScoreArgs& a, int g, int64_t c0, int j0, int c16, int q4,
+                                           bf16x8 (&b)[4]) {
   int64_t rowc = c0 + j0 + c16;
   rowc = rowc < a.c_rows ? rowc : a.c_rows - 1;
   const uint16_t* kp = a.kc + ((int64_t)g * a.c_rows + rowc) * kHeadDim + 8 * q4;
-  bf16x8 b[4];
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) b[ks] = as_bf16x8(ldg16(kp + 32 * ks));
+}
+// S^T chunk: heads (rows) x 16 keys (columns) of one query row.
+__device__ __forceinline__ floatx4 chunk_scores(const bf16x8 (&qa)[4], const bf16x8 (&b)[4]) {
   floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) acc = mfma16(qa[ks], b[ks], acc);
@@ -471,15 +474,29 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_lse_split_kernel(
     m[i] = -__builtin_inff();
     sm[i] = 0.f;
   }
-  for (int ch = ca + wave; ch < cb; ch += kSplitScoreWaves) {
-    const floatx4 acc = split_chunk(a, qa, g, r.c0, 16 * ch, c16, q4);
-    const bool ok = 16 * ch + c16 < r.nv;
+  // This wave's chunks: ca + wave, ca + wave + 4, ...; four of them in flight.
+  constexpr int W = kSplitScoreWaves;
+  bf16x8 ring[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (ca + wave + W * i < cb) chunk_keys(a, g, r.c0, 16 * (ca + wave + W * i), c16, q4, ring[i]);
+  for (int base = ca + wave; base < cb; base += 4 * W) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (ok) {
-        const float mn = fmaxf(m[i], acc[i]);
-        sm[i] = sm[i] * fast_exp2((m[i] - mn) * a.c) + fast_exp2((acc[i] - mn) * a.c);
-        m[i] = mn;
+      const int ch = base + W * i;
+      if (ch < cb) {
+        const bf16x8 b[4] = {ring[i][0], ring[i][1], ring[i][2], ring[i][3]};
+        if (ch + 4 * W < cb) chunk_keys(a, g, r.c0, 16 * (ch + 4 * W), c16, q4, ring[i]);
+        const floatx4 acc = chunk_scores(qa, b);
+        const bool ok = 16 * ch + c16 < r.nv;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (ok) {
+            const float mn = fmaxf(m[j], acc[j]);
+            sm[j] = sm[j] * fast_exp2((m[j] - mn) * a.c) + fast_exp2((acc[j] - mn) * a.c);
+            m[j] = mn;
+          }
+        }
       }
     }
   }
@@ -528,26 +545,8 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_split_kern
   const int wave = tid >> 6;
   SplitRow r;
   if (!split_row(a, row, r)) return;
-  // LSE of the lane's four heads (in log2 units, scaled) from the partials.
-  float Lc[4];
-  {
-    const float* src = a.part + ((int64_t)row * a.h_kv + g) * a.splits * 32;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int h = 4 * q4 + i;
-      float mm = -__builtin_inff();
-      for (int p = 0; p < a.splits; ++p) mm = fmaxf(mm, src[p * 32 + 2 * h]);
-      float ss = 0.f;
-      for (int p = 0; p < a.splits; ++p) {
-        const float m2 = src[p * 32 + 2 * h];
-        if (m2 > -__builtin_inff()) ss += src[p * 32 + 2 * h + 1] * fast_exp2((m2 - mm) * a.c);
-      }
-      Lc[i] = ss > 0.f ? mm * a.c + __builtin_amdgcn_logf(ss) : __builtin_inff();
-    }
-  }
-  bf16x8 qa[4];
-  load_q(a, row, g, c16, q4, qa);
-  // Windows overlapping candidate blocks n_init .. bt - n_local: chunks of 16.
+  // Windows overlapping candidate blocks n_init .. bt - n_local: chunks of 16;
+  // this wave takes a contiguous run [ca, cb) of them.
   const int b_hi = r.bt - a.n_local;
   const int cfirst = max(0, 4 * a.n_init - 1) >> 4;
   const int clast = (4 * b_hi + 3) >> 4;   // inclusive
@@ -556,28 +555,65 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_split_kern
   const int cb0 = cfirst + (int)((int64_t)nch * (sp + 1) / a.splits);
   const int ca = ca0 + (int)((int64_t)(cb0 - ca0) * wave / kSplitScoreWaves);
   const int cb = ca0 + (int)((int64_t)(cb0 - ca0) * (wave + 1) / kSplitScoreWaves);
+  // Keys in flight first: the chunk before the run (its last window feeds
+  // the first quad) and the first four chunks of the run.
+  bf16x8 prevk[4], ring[4][4];
+  if (ca < cb && ca > 0) chunk_keys(a, g, r.c0, 16 * (ca - 1), c16, q4, prevk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (ca + i < cb) chunk_keys(a, g, r.c0, 16 * (ca + i), c16, q4, ring[i]);
+  // The row's LSE partials, fetched by the whole workgroup at once.
+  __shared__ float parts[kSplitMaxSplits * 32];
+  {
+    const float* src = a.part + ((int64_t)row * a.h_kv + g) * a.splits * 32;
+    for (int i = tid; i < a.splits * 32; i += 64 * kSplitScoreWaves) parts[i] = src[i];
+  }
+  __syncthreads();
   if (ca >= cb) return;
-  auto chunk_sum = [&](int ch) -> float {
-    const floatx4 acc = split_chunk(a, qa, g, r.c0, 16 * ch, c16, q4);
+  bf16x8 qa[4];
+  load_q(a, row, g, c16, q4, qa);
+  // LSE of the lane's four heads (log2 units, scaled).
+  float Lc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * q4 + i;
+    float mm = -__builtin_inff();
+    for (int p = 0; p < a.splits; ++p) mm = fmaxf(mm, parts[p * 32 + 2 * h]);
+    float ss = 0.f;
+    for (int p = 0; p < a.splits; ++p) {
+      const float m2 = parts[p * 32 + 2 * h];
+      if (m2 > -__builtin_inff()) ss += parts[p * 32 + 2 * h + 1] * fast_exp2((m2 - mm) * a.c);
+    }
+    Lc[i] = ss > 0.f ? mm * a.c + __builtin_amdgcn_logf(ss) : __builtin_inff();
+  }
+  auto chunk_sum = [&](int ch, const bf16x8 (&b)[4]) -> float {
+    const floatx4 acc = chunk_scores(qa, b);
     float sum = fast_exp2(fmaf(acc[0], a.c, -Lc[0]));
 #pragma unroll
     for (int i = 1; i < 4; ++i) sum += fast_exp2(fmaf(acc[i], a.c, -Lc[i]));
     sum = sum_x16(sum_x32(sum));   // all heads of the group: lane c16 -> key 16 ch + c16
     return 16 * ch + c16 < r.nv ? sum : 0.f;
   };
-  // Window 16 ca - 1 (the last of the previous chunk) feeds the first quad.
   float carry = 0.f;
-  if (ca > 0) carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(chunk_sum(ca - 1)), 15));
+  if (ca > 0) carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(chunk_sum(ca - 1, prevk)), 15));
   float* bsr = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld;
-  for (int ch = ca; ch < cb; ++ch) {
-    const float S = chunk_sum(ch);
-    const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));       // quad_perm 1,0,3,2
-    const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));    // quad_perm 2,3,0,1
-    const float prev = dpp_f32<0x138>(carry, S);          // wave_shr:1
-    carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 15));
-    if (lane < 16 && (lane & 3) == 0) {
-      const int b = 4 * ch + (lane >> 2);
-      if (b >= a.n_init && b <= b_hi && b < a.bs_ld) bsr[b] = fmaxf(qm, prev);
+  for (int base = ca; base < cb; base += 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = base + i;
+      if (ch < cb) {
+        const bf16x8 b[4] = {ring[i][0], ring[i][1], ring[i][2], ring[i][3]};
+        if (ch + 4 < cb) chunk_keys(a, g, r.c0, 16 * (ch + 4), c16, q4, ring[i]);   // four ahead
+        const float S = chunk_sum(ch, b);
+        const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));       // quad_perm 1,0,3,2
+        const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));    // quad_perm 2,3,0,1
+        const float prev = dpp_f32<0x138>(carry, S);          // wave_shr:1
+        carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 15));
+        if (lane < 16 && (lane & 3) == 0) {
+          const int b = 4 * ch + (lane >> 2);
+          if (b >= a.n_init && b <= b_hi && b < a.bs_ld) bsr[b] = fmaxf(qm, prev);
+        }
+      }
     }
   }
 }

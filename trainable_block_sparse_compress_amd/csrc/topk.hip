@@ -171,3 +171,202 @@ hipError_t launch_topk(const TopkArgs& a, int batch, int h_kv, int max_seqlen_q,
 }
 
 }  // namespace infllmv2
+
+// ---------------------------------------------------------------------------
+// Row path: one workgroup of 256 threads per (query row, KV group), for
+// launches with few rows (decode).  Thread i owns the PER consecutive
+// candidates PER*i .. PER*i+PER-1, so candidate order is thread order; the
+// same radix select runs on a shared 256-bin histogram, and two workgroup
+// scans (ties, then selected counts) give every thread its output slots.
+// ---------------------------------------------------------------------------
+namespace infllmv2 {
+namespace {
+
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ int seq_of_row_t(const TopkArgs& a, int64_t row) {
+  int lo = 0, hi = a.batch - 1;
+  if (hi < 0) return -1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (a.cu_q[mid] <= row) lo = mid;
+    else hi = mid - 1;
+  }
+  const SeqRange r = seq_range(a.cu_q, a.used_q, lo);
+  return (row >= r.start && row < (int64_t)r.start + r.len) ? lo : -1;
+}
+
+// Exclusive prefix over the workgroup's threads; `total` gets the sum.
+__device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  __syncthreads();   // wsum free from any earlier use
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / 64; ++w) {
+    const int x = wsum[w];
+    before += w < wave ? x : 0;
+    total += x;
+  }
+  return before + incl - v;
+}
+
+template <int PER>
+__global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(TopkArgs a) {
+  __shared__ uint32_t hist[256];
+  __shared__ int wsum[kRowThreads / 64];
+  __shared__ uint32_t ext[2][kRowThreads / 64];
+  __shared__ int pick[2];
+  const int64_t row = blockIdx.x;
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s = seq_of_row_t(a, row);
+  if (s < 0) return;
+  const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
+  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
+  const int t = rk.len - rq.len + (int)(row - rq.start);
+  if (t < 0) return;
+  const int bt = t / kBlock;
+  const int n_sel = a.n_init + a.n_local + a.n_topk;
+  int32_t* out = a.idx + ((int64_t)g * a.rows_q + row) * n_sel;
+  const int lo = a.n_init;
+  const int hi = (int)min((int64_t)(bt - a.n_local), a.bs_ld - 1);
+  const int nc = hi - lo + 1;
+  if (nc <= a.n_topk) {
+    for (int e = tid; e < n_sel; e += kRowThreads) out[e] = e <= bt ? e : -1;
+    return;
+  }
+  const float* row_bs = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld + lo;
+  uint32_t key[PER];
+  uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int c = PER * tid + p;
+    key[p] = 0;
+    if (c < nc) {
+      key[p] = __float_as_uint(row_bs[c]) + 1u;
+      kmax = max(kmax, key[p]);
+      kmin = min(kmin, key[p]);
+    }
+  }
+  for (int off = 32; off >= 1; off >>= 1) {
+    kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, off));
+    kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, off));
+  }
+  if (lane == 0) {
+    ext[0][wave] = kmax;
+    ext[1][wave] = kmin;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kRowThreads / 64; ++w) {
+    kmax = max(kmax, ext[0][w]);
+    kmin = min(kmin, ext[1][w]);
+  }
+  const uint32_t diff = kmax ^ kmin;
+  const int top_bit = diff ? 31 - __clz((int)diff) : 0;
+  uint32_t prefix = diff ? (kmax & ~((top_bit >= 31) ? 0xFFFFFFFFu : ((2u << top_bit) - 1u))) : kmax;
+  uint32_t pmask = diff ? ~((top_bit >= 31) ? 0xFFFFFFFFu : ((2u << top_bit) - 1u)) : 0xFFFFFFFFu;
+  int kk = a.n_topk;
+  if (diff) {
+    for (int hb = top_bit; hb >= 0; hb -= 8) {
+      const int lob = max(0, hb - 7);
+      const int width = hb - lob + 1;
+      const uint32_t dmask = (1u << width) - 1u;
+      hist[tid] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int p = 0; p < PER; ++p)
+        if (key[p] != 0 && (key[p] & pmask) == prefix) atomicAdd(&hist[(key[p] >> lob) & dmask], 1u);
+      __syncthreads();
+      if (wave == 0) {
+        uint32_t h4[4], local = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          h4[b] = hist[lane * 4 + b];
+          local += h4[b];
+        }
+        uint32_t suffix = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+          const uint32_t o = (uint32_t)__shfl_down((int)suffix, off);
+          if (lane + off < 64) suffix += o;
+        }
+        uint32_t cum = suffix - local;
+        int found = -1, newk = 0;
+#pragma unroll
+        for (int b = 3; b >= 0; --b) {
+          if (found < 0 && cum < (uint32_t)kk && (uint32_t)kk <= cum + h4[b]) {
+            found = lane * 4 + b;
+            newk = kk - (int)cum;
+          }
+          cum += h4[b];
+        }
+        const uint64_t ball = __ballot(found >= 0);
+        const int src = __ffsll((unsigned long long)ball) - 1;
+        if (lane == src) {
+          pick[0] = found;
+          pick[1] = newk;
+        }
+      }
+      __syncthreads();
+      const int digit = pick[0];
+      kk = pick[1];
+      prefix |= ((uint32_t)digit & dmask) << lob;
+      pmask |= dmask << lob;
+      __syncthreads();   // hist and pick are rewritten by the next pass
+    }
+  }
+  const uint32_t T = prefix;
+
+  // Ties: the lowest-index kk keys equal to T are taken.
+  int n_eq = 0, n_gt = 0;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    n_eq += (key[p] == T && key[p] != 0);
+    n_gt += key[p] > T;
+  }
+  int tot;
+  const int eq_before = wg_exclusive_scan(n_eq, wsum, tot);
+  const int n_take = n_gt + max(0, min(n_eq, kk - eq_before));
+  int pos = wg_exclusive_scan(n_take, wsum, tot);
+  const int n_init_eff = min(a.n_init, bt + 1);
+  for (int e = tid; e < n_init_eff; e += kRowThreads) out[e] = e;
+  pos += n_init_eff;
+  int eq_rank = eq_before;
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const bool eq = key[p] == T && key[p] != 0;
+    const bool take = key[p] > T || (eq && eq_rank < kk);
+    eq_rank += eq;
+    if (take) {
+      if (pos < n_init_eff + a.n_topk) out[pos] = lo + PER * tid + p;
+      ++pos;
+    }
+  }
+  const int base = n_init_eff + a.n_topk;
+  for (int r = tid; r < a.n_local; r += kRowThreads) out[base + r] = bt - a.n_local + 1 + r;
+}
+
+}  // namespace
+
+hipError_t launch_topk_rows(const TopkArgs& a, int h_kv, int max_blocks, hipStream_t st) {
+  dim3 grid((unsigned)a.rows_q, h_kv);
+  const int need = (max_blocks + kRowThreads - 1) / kRowThreads;
+  if (need <= 4) hipLaunchKernelGGL(topk_rows_kernel<4>, grid, dim3(kRowThreads), 0, st, a);
+  else if (need <= 8) hipLaunchKernelGGL(topk_rows_kernel<8>, grid, dim3(kRowThreads), 0, st, a);
+  else if (need <= 16) hipLaunchKernelGGL(topk_rows_kernel<16>, grid, dim3(kRowThreads), 0, st, a);
+  else if (need <= 32) hipLaunchKernelGGL(topk_rows_kernel<32>, grid, dim3(kRowThreads), 0, st, a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+}  // namespace infllmv2
