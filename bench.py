@@ -129,11 +129,20 @@ def main():
                          "kernel of known size, to calibrate HBM byte counters)")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="also time the dense causal kernel at the same length (context)")
+    ap.add_argument("--workload", choices=["prefill", "decode", "varlen"], default="prefill",
+                    help="prefill (default): one 128K sequence; decode: 16 sequences x 128K "
+                         "cache, one token each per step; varlen: 65536 packed tokens of mixed "
+                         "lengths through the dense/sparse switch")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
                                    "(multi-GPU sharding is described in DESIGN.md, not built)"}))
         sys.exit(2)
+
+    if args.workload == "decode":
+        return bench_decode(args)
+    if args.workload == "varlen":
+        return bench_varlen(args)
 
     import torch
 
@@ -248,6 +257,179 @@ def main():
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         res["cpu_baseline"] = cpu_baseline(inp, n, h_q, h_kv, args.lse, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def bench_decode(args):
+    """Decode: batch 16, a 128K-token cache per sequence, one new token per
+    sequence per step (incremental compress_k, select_blocks, sparse_attn:
+    the split-K path).  Timed per step with HIP events around the library
+    calls; the caller's cache append is outside the timed region."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    batch, len0, h_q, h_kv, d = 16, args.seq, 32, 2, 128
+    nsteps = args.warmup + args.steps
+    print(f"[bench] decode inputs batch={batch} cache={len0}", file=sys.stderr, flush=True)
+    inp = D.make_decode(4, batch, len0, nsteps, h_q, h_kv, d, n_needles=32)
+    cap = (len0 + nsteps + 63) // 64 * 64
+    cfg = P.SparseConfig(lse_mode=args.lse)
+    dec = P.DecodeState(batch, cap, h_q, h_kv, cfg)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    kc, vc = dev(inp.k_cache[:, :len0]), dev(inp.v_cache[:, :len0])
+    dec.fill([kc[s] for s in range(batch)], [vc[s] for s in range(batch)], [len0] * batch)
+    del kc, vc
+    qs, ks, vs = dev(inp.q_steps), dev(inp.k_steps), dev(inp.v_steps)
+    out = torch.empty((batch, h_q, d), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+    t_step, t_sel, t_attn = [], [], []
+    print("[bench] decode steps", file=sys.stderr, flush=True)
+    for i in range(nsteps):
+        old = dec.append(ks[i], vs[i])
+        dec.step_prepare(old)
+        q_new = qs[i].contiguous()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        c, mx = cfg, max(dec.lens)
+        ev[0].record(stream)
+        B.compress_k(dec.k_cache, dec.cu_k, dec.used_k, batch, mx, c.c1[0], c.c1[1], dec.cu_c1,
+                     dec.kc1, cmp_begin=dec.begin1, max_new=1)
+        if dec.approx:
+            B.compress_k(dec.k_cache, dec.cu_k, dec.used_k, batch, mx, c.c2[0], c.c2[1], dec.cu_c2,
+                         dec.kc2, cmp_begin=dec.begin2, max_new=1)
+        ev[1].record(stream)
+        B.select_blocks(q_new, dec.kc1, dec.kc2, dec.cu_q, dec.used_q, dec.cu_k, dec.used_k,
+                        dec.cu_c1, dec.cu_c2, batch, 1, mx, c.n_init, c.n_local, c.n_topk,
+                        c.scale(d), dec.block_idx, dec.ws_select)
+        ev[2].record(stream)
+        B.sparse_attn(q_new, dec.k_cache, dec.vt_cache, dec.cu_q, dec.used_q, dec.cu_k, dec.used_k,
+                      batch, 1, mx, dec.block_idx, c.n_init, c.n_local, c.scale(d), out, None,
+                      dec.ws_attn, v_seq_stride=cap)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        if i >= args.warmup:
+            t_step.append(ev[0].elapsed_time(ev[3]))
+            t_sel.append(ev[1].elapsed_time(ev[2]))
+            t_attn.append(ev[2].elapsed_time(ev[3]))
+    ms = float(np.mean(t_step))
+    # Algorithmic HBM bytes per step: the stage-1 keys read once (scoring),
+    # the selected K and V blocks of every sequence and KV group, the block
+    # scores written and read, and the block lists.
+    n1 = (len0 - 32) // 16 + 1
+    nblk = (len0 + 63) // 64
+    kc1_bytes = batch * h_kv * n1 * d * 2
+    kv_bytes = batch * h_kv * cfg.n_sel * 64 * d * 2 * 2
+    bs_bytes = 2 * batch * h_kv * nblk * 4 + batch * h_kv * cfg.n_sel * 4
+    step_bytes = kc1_bytes + kv_bytes + bs_bytes
+    gbs = step_bytes / (ms * 1e-3) / 1e9
+    res = {
+        "metric": "sparse-attn decode tokens/s (batch 16, 128K cache, 32q/2kv, d128, |I|=96)",
+        "value": batch / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 cache and step tokens, 32 needle blocks/seq",
+        "config": {"workload": f"decode, batch {batch}, cache {len0} per sequence, one token per "
+                               "sequence per step", "h_q": h_q, "h_kv": h_kv, "head_dim": d,
+                   "n_init": 1, "n_local": 32, "n_topk": 63, "lse": args.lse},
+        "ms_select_blocks": float(np.mean(t_sel)), "ms_sparse_attn": float(np.mean(t_attn)),
+        "roofline": {"bound": "hbm", "kernel": "whole decode step (compress_k + select_blocks + "
+                                                "sparse_attn)",
+                     "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                     "bytes_per_step": step_bytes, "traffic": None},
+    }
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline_decode(inp, batch, len0, h_q, h_kv, args.lse,
+                                                  args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline_decode(inp, batch, len0, h_q, h_kv, lse_mode, budget_s=15.0):
+    """The fp64 oracle on the first decode step: stage-1 (and coarse) keys of
+    the caches, then selection + attention of each sequence's new token until
+    the budget is spent; extrapolated to one whole step of the batch.  The
+    compression of the whole cache is a one-time cost and not counted."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle.reference as R
+    p = R.Params(lse_mode=lse_mode, round_kc=True)
+    G = h_q // h_kv
+    done, t_rows = 0, 0.0
+    with threadpool_limits(limits=1):
+        for s in range(batch):
+            K = np.concatenate([inp.k_cache[s, :len0], inp.k_steps[0, s][None]], axis=0)
+            V = np.concatenate([inp.v_cache[s, :len0], inp.v_steps[0, s][None]], axis=0)
+            KC1 = R.compress_keys(K, 32, 16, True)
+            KC2 = R.compress_keys(K, 128, 64, True) if lse_mode == "approx" else None
+            Kf, Vf = R.as_f64(K), R.as_f64(V)
+            t0 = time.perf_counter()
+            sel, _ = R.select_token(inp.q_steps[0, s], len0, KC1, KC2, G, p)
+            R.attend_token(inp.q_steps[0, s], len0, Kf, Vf, sel, G, p)
+            t_rows += time.perf_counter() - t0
+            done += 1
+            if t_rows > budget_s:
+                break
+    per = t_rows / done
+    return {"value": 1.0 / per, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 oracle, 1 BLAS thread: selection + attention of the new token of "
+                      f"{done} of {batch} sequences at position {len0} ({t_rows:.1f} s); cache "
+                      f"compression not counted"}
+
+
+def bench_varlen(args):
+    """Varlen prefill: 65536 packed tokens, lengths drawn from the 0-4K, 4-12K,
+    12-24K and 24-32K buckets; sequences <= 8192 take dense attention, the
+    rest the sparse path (one SwitchPlan call per step)."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    h_q, h_kv, d = 32, 2, 128
+    lengths = D.varlen_lengths(5)
+    print(f"[bench] varlen inputs: {len(lengths)} sequences", file=sys.stderr, flush=True)
+    inp = D.make_prefill(5, lengths, h_q, h_kv, d)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    cfg = P.SparseConfig(lse_mode=args.lse)
+    plan = P.SwitchPlan(lengths, h_q, h_kv, cfg)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.run(q, k, v, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.run(q, k, v, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    total = sum(lengths)
+    flops = 0.0
+    for n in lengths:
+        if n <= cfg.threshold:
+            flops += 4.0 * d * h_q * n * (n + 1) / 2
+        else:
+            w = algorithmic_work(n, h_q, h_kv, d)
+            flops += w["attn_flops"] + w["blocks_flops"] + (
+                w["lse_exact_flops"] if args.lse == "exact" else w["lse_approx_flops"])
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "varlen prefill tokens/s (65536 packed tokens, 0-32K mix, 32q/2kv, d128)",
+        "value": total / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded i.i.d. N(0,1) bf16 Q/K/V",
+        "config": {"workload": f"varlen prefill, {len(lengths)} sequences, {total} tokens "
+                               "(<= 8192 dense, longer sparse |I| = 96)",
+                   "lengths": lengths, "lse": args.lse},
+        "roofline": {"bound": "mfma", "kernel": "whole step (all kernels)", "achieved": tf,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+    }
     print(json.dumps(res), flush=True)
 
 
