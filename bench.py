@@ -129,10 +129,14 @@ def main():
                          "kernel of known size, to calibrate HBM byte counters)")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="also time the dense causal kernel at the same length (context)")
-    ap.add_argument("--workload", choices=["prefill", "decode", "varlen"], default="prefill",
+    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep"],
+                    default="prefill",
                     help="prefill (default): one 128K sequence; decode: 16 sequences x 128K "
                          "cache, one token each per step; varlen: 65536 packed tokens of mixed "
-                         "lengths through the dense/sparse switch")
+                         "lengths through the dense/sparse switch; sweep: the prefill at several "
+                         "selection sizes |I| against the dense kernel at the same length")
+    ap.add_argument("--sel", type=str, default="16,32,64,96",
+                    help="sweep: selection sizes |I| (1 init block, |I|//3 local, rest top-k)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
@@ -143,6 +147,8 @@ def main():
         return bench_decode(args)
     if args.workload == "varlen":
         return bench_varlen(args)
+    if args.workload == "sweep":
+        return bench_sweep(args)
 
     import torch
 
@@ -428,6 +434,102 @@ def bench_varlen(args):
                    "lengths": lengths, "lse": args.lse},
         "roofline": {"bound": "mfma", "kernel": "whole step (all kernels)", "achieved": tf,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def sweep_split(n_sel):
+    """Selection size |I| -> (n_init, n_local, n_topk): one init block, a
+    third of |I| as the local window (32 of 96 at the headline size), the
+    rest top-k."""
+    n_local = n_sel // 3
+    return 1, n_local, n_sel - 1 - n_local
+
+
+def bench_sweep(args):
+    """The prefill path at several selection sizes |I| (the pages compare the
+    kernel against dense attention at 16 selected blocks), each against the
+    dense causal kernel at the same length.  Per |I|: compress_k +
+    select_blocks + sparse_attn timed with HIP events, algorithmic flops of
+    the attention kernel, and its speedup over the dense kernel."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    n, h_q, h_kv, d = args.seq, 32, 2, 128
+    sizes = [int(x) for x in args.sel.split(",") if x.strip()]
+    print(f"[bench] sweep inputs n={n} |I| in {sizes}", file=sys.stderr, flush=True)
+    inp = D.make_prefill(3, n, h_q, h_kv, d, n_needles=32)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    vt = v.permute(1, 2, 0).contiguous().view(h_kv, d, 1, n)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    base = P.SparseConfig(lse_mode=args.lse)
+    dplan = P.DensePlan([0], [n], [0], [n], n, h_q, h_kv, base, "cuda", d)
+    print("[bench] dense kernel", file=sys.stderr, flush=True)
+    dms = timed(lambda: B.dense_attn(q, k, vt, dplan.cu_q, dplan.used_q, dplan.cu_k,
+                                     dplan.used_k, 1, n, n, base.scale(d), out, None, None,
+                                     v_seq_stride=n), max(1, args.dense_steps or 2))
+    dflops = 4.0 * d * h_q * (n * (n + 1) / 2)
+    rows = []
+    for n_sel in sizes:
+        ni, nl, nt = sweep_split(n_sel)
+        cfg = P.SparseConfig(n_init=ni, n_local=nl, n_topk=nt, lse_mode=args.lse)
+        plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
+        print(f"[bench] |I| = {n_sel} ({ni} + {nl} + {nt})", file=sys.stderr, flush=True)
+        for _ in range(args.warmup):
+            plan.compress(k)
+            plan.select(q)
+        run_attn = lambda: B.sparse_attn(q, k, vt, plan.cu_q, plan.used_q, plan.cu_k,
+                                         plan.used_k, 1, n, n, plan.block_idx, cfg.n_init,
+                                         cfg.n_local, cfg.scale(d), out, None, None,
+                                         v_seq_stride=n)
+        ms_c = timed(lambda: plan.compress(k), args.steps)
+        ms_s = timed(lambda: plan.select(q), args.steps)
+        ms_a = timed(run_attn, args.steps)
+        w = algorithmic_work(n, h_q, h_kv, d, ni, nl, nt)
+        lse = w["lse_exact_flops"] if args.lse == "exact" else w["lse_approx_flops"]
+        ms = ms_c + ms_s + ms_a
+        rows.append({"n_sel": n_sel, "split": [ni, nl, nt], "ms_step": ms,
+                     "tokens_per_s": n / (ms * 1e-3), "ms_compress_k": ms_c,
+                     "ms_select_blocks": ms_s, "ms_sparse_attn": ms_a,
+                     "attn_tflops": w["attn_flops"] / (ms_a * 1e-3) / 1e12,
+                     "step_mfma_frac": (w["attn_flops"] + lse + w["blocks_flops"])
+                     / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+                     "attn_speedup_vs_dense_kernel": dms / ms_a,
+                     "step_speedup_vs_dense_kernel": dms / ms})
+        del plan
+    head = next((r for r in rows if r["n_sel"] == 96), rows[-1])
+    res = {
+        "metric": f"sparse-attn prefill tokens/s by selection size |I| at n={n} "
+                  "(32q/2kv, d128) vs the dense kernel",
+        "value": head["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_step"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 Q/K/V with 32 planted needle blocks",
+        "config": {"workload": f"sparse prefill at |I| in {sizes}, one layer, n={n}",
+                   "seq_len": n, "lse": args.lse, "value_is": f"|I| = {head['n_sel']}"},
+        "dense_attn_ms": dms, "dense_attn_tflops": dflops / (dms * 1e-3) / 1e12,
+        "sweep": rows,
+        "roofline": {"bound": "mfma", "kernel": f"attn_kernel at |I| = {head['n_sel']}",
+                     "achieved": head["attn_tflops"], "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": head["attn_tflops"] / PEAK_BF16_TFLOPS,
                      "traffic": None},
     }
     print(json.dumps(res), flush=True)

@@ -366,7 +366,10 @@ struct Attn {
   }
 
   // One window of blocks [w0, w1): build the token masks, run the shared
-  // phase over the popular blocks, then the private phase.
+  // phase over the popular blocks, then the private phase.  kPair: balance
+  // the shared list (left out of the multi-window kernel, whose loop leaves
+  // no registers for it).
+  template <bool kPair>
   __device__ __forceinline__ void window(AttnLds& sh, int w0, int w1, int nq, int pos0, int i0,
                                          bool dense, int tid) {
     // 1. init / local (dense: every causal block), by arithmetic.
@@ -432,6 +435,47 @@ struct Attn {
       n_ent += total;
     }
     __syncthreads();
+    // 3b. order the shared list for balance: within each run of 64 entries an
+    //     entry is followed by the first later one whose tokens lie in other
+    //     waves (else by the next one), so the two blocks of a batch tend to
+    //     occupy different waves.  Runs are 64 entries, so batches of two
+    //     never straddle them.
+    if (kPair && !dense) {
+      for (int c = wave; 64 * c < n_ent; c += kAttnWaves) {
+        const int cnt = min(64, n_ent - 64 * c);
+        const bool ok = lane < cnt;
+        const int32_t ubv = ok ? sh.ub[64 * c + lane] : 0;
+        const uint32_t umv = ok ? sh.um[64 * c + lane] : 0u;
+        uint32_t wm = 0;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w)
+          wm |= (uint32_t)(((umv >> (kTPW * w)) & ((1u << kTPW) - 1u)) != 0u) << w;
+        const uint64_t valid = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
+        uint64_t used = 0;
+        int dest = 0, p = 0;
+        for (int i = 0; i < cnt; ++i) {
+          if ((used >> i) & 1ull) continue;
+          used |= 1ull << i;
+          dest = lane == i ? p : dest;
+          ++p;
+          const uint32_t aw = __builtin_amdgcn_readlane(wm, i);
+          const uint64_t later = valid & ~used & ~((2ull << i) - 1ull);
+          uint64_t cand = __ballot((wm & aw) == 0u) & later;
+          if (cand == 0) cand = later;
+          if (cand != 0) {
+            const int j = (int)__builtin_ctzll(cand);
+            used |= 1ull << j;
+            dest = lane == j ? p : dest;
+            ++p;
+          }
+        }
+        if (ok) {
+          sh.ub[64 * c + dest] = ubv;
+          sh.um[64 * c + dest] = umv;
+        }
+      }
+      __syncthreads();
+    }
     // 4. shared phase: walk the list; the next batch's staging loads are in
     //    flight while the current one computes.
     if (n_ent > 0) {
@@ -565,10 +609,10 @@ struct Attn {
     // both phases' address registers live at once).  Blocks past the V^T row
     // are never attended, so clamping to kWin there loses nothing.
     if constexpr (!kMulti) {
-      window(sh, 0, min(bt_last + 1, kWin), nq, pos0, i0, dense, tid);
+      window<true>(sh, 0, min(bt_last + 1, kWin), nq, pos0, i0, dense, tid);
     } else {
       for (int w0 = 0; w0 <= bt_last; w0 += kWin) {
-        window(sh, w0, min(bt_last + 1, w0 + kWin), nq, pos0, i0, dense, tid);
+        window<false>(sh, w0, min(bt_last + 1, w0 + kWin), nq, pos0, i0, dense, tid);
         __syncthreads();   // mask, lists and LDS are reused by the next window
       }
     }
