@@ -30,7 +30,11 @@ Readings of points the pages leave open (each is stated where it is used):
     stride 4, one window of left padding): exactly the windows that overlap
     the block's tokens;
   * top-k ties break toward the lower block index;
-  * the approximate LSE is the plain log-sum-exp over visible coarse windows.
+  * the approximate LSE is the plain log-sum-exp over visible coarse windows;
+  * gradients (training, [R] "训练是怎么做的": the sparse attention is trained
+    with the plain next-token objective) treat the block sets as constants:
+    selection is a top-k, piecewise constant in q and k, and its scores
+    reach no output.
 
 Positions are per sequence and 0-based; with ``len_q`` queries and ``len_k``
 keys, query i sits at position ``len_k - len_q + i`` (bottom-right causal).
@@ -47,6 +51,7 @@ __all__ = [
     "compress_keys_incremental", "logits", "lse_exact", "lse_approx", "shared_scores",
     "block_scores", "select_from_scores", "select_token", "attend_token", "dense_token",
     "prefill_select", "prefill_attend", "dense_prefill", "candidate_range",
+    "attend_token_grad", "attention_grad",
 ]
 
 
@@ -361,3 +366,80 @@ def dense_prefill(Q, K, V, G: int, scale: float, positions=None):
     if positions is None:
         positions = range(n_k - n_q, n_k)
     return {t: dense_token(np.asarray(Q)[t - (n_k - n_q)], t, Kf, Vf, G, scale) for t in positions}
+
+
+# --------------------------------------------------------------------------
+# Gradients of the sparse attention, block sets held fixed  [R] (training:
+# "训练是怎么做的", long-context fine-tuning through the sparse attention)
+# --------------------------------------------------------------------------
+#
+# For one query and head with logits z_u = scale * q . k_u over its key set
+# T, probabilities P_u = exp(z_u) / sum_w exp(z_w) and output o = sum_u P_u v_u,
+# an upstream gradient dO = dl/do gives, by the chain rule through the
+# softmax Jacobian dP_u/dz_w = P_u (delta_uw - P_w):
+#   dl/dv_u = P_u dO
+#   dl/dz_u = P_u (dO . v_u - dO . o)
+#   dl/dq   = scale * sum_u dl/dz_u k_u,   dl/dk_u = scale * dl/dz_u q.
+# Query heads of one group add their dk, dv into the group's shared K, V.
+
+def _attend_grad(q, dout, K, V, keys_per_group, G: int, scale: float):
+    q, dout = as_f64(q), as_f64(dout)
+    h_q, d = q.shape
+    dq = np.zeros((h_q, d))
+    dk = [np.zeros((len(u), d)) for u in keys_per_group]
+    dv = [np.zeros((len(u), d)) for u in keys_per_group]
+    for h in range(h_q):
+        g = h // G
+        u = keys_per_group[g]
+        if len(u) == 0:
+            continue
+        Ku, Vu = K[u, g], V[u, g]
+        z = scale * (Ku @ q[h])
+        w = np.exp(z - z.max())
+        P = w / w.sum()
+        o = P @ Vu
+        dz = P * (Vu @ dout[h] - dout[h] @ o)
+        dq[h] = scale * (dz @ Ku)
+        dk[g] += scale * np.outer(dz, q[h])
+        dv[g] += np.outer(P, dout[h])
+    return dq, dk, dv
+
+
+def _keys_of(blocks, t: int, B: int):
+    """Keys u <= t of the given blocks, read as a set (-1 and repeats skipped)."""
+    bs = sorted({b for b in blocks if 0 <= b <= t // B})
+    return np.array([x for b in bs for x in range(b * B, min((b + 1) * B, t + 1))], dtype=np.int64)
+
+
+def attend_token_grad(q, dout, t: int, K, V, blocks, G: int, p: Params):
+    """Gradients of sum(dout * o) for the sparse attention of query t (see
+    attend_token).  Returns dq [h_q, d] and, per KV group, (keys, dk rows,
+    dv rows) of its contribution to the key gradients."""
+    B = p.block_size
+    keys = [_keys_of(bl, t, B) for bl in blocks]
+    dq, dk, dv = _attend_grad(q, dout, K, V, keys, G, _scale(p, K.shape[2]))
+    return dq, [(keys[g], dk[g], dv[g]) for g in range(len(keys))]
+
+
+def attention_grad(Q, K, V, dO, G: int, p: Params, idx_by_pos=None, dense: bool = False):
+    """Whole-sequence gradients (dQ, dK, dV) of sum(dO * O) for one sequence:
+    queries are the last len_q positions of the len_k keys; ``idx_by_pos``
+    maps each position to its per-group block lists (the selection, held
+    fixed); ``dense`` uses every causal key instead."""
+    Kf, Vf = as_f64(K), as_f64(V)
+    Qa, dOa = np.asarray(Q), np.asarray(dO)
+    n_k, n_q = Kf.shape[0], Qa.shape[0]
+    h_kv = Kf.shape[1]
+    dQ = np.zeros(Qa.shape, dtype=np.float64)
+    dK = np.zeros(Kf.shape)
+    dV = np.zeros(Vf.shape)
+    nblk = (n_k + p.block_size - 1) // p.block_size
+    for i in range(n_q):
+        t = n_k - n_q + i
+        blocks = [list(range(nblk))] * h_kv if dense else idx_by_pos[t]
+        dq, parts = attend_token_grad(Qa[i], dOa[i], t, Kf, Vf, blocks, G, p)
+        dQ[i] = dq
+        for g, (u, dk, dv) in enumerate(parts):
+            dK[u, g] += dk
+            dV[u, g] += dv
+    return dQ, dK, dV

@@ -352,12 +352,100 @@ def pin_cost_identities():
     return abs(unfused / (h_q * n * n / 16) - 1) < 1e-3 and unfused / fused == G
 
 
+def _grad_case(seed=31, n=150, h_q=4, h_kv=2, d=8, B=16, with_sets=True):
+    """Tiny sequence with random per-token block sets (own block always in)."""
+    Q, K, V = _tiny(seed, n=n, h_q=h_q, h_kv=h_kv, d=d)
+    dO = _rng(seed + 1).standard_normal((n, h_q, d))
+    p = R.Params(block_size=B)
+    g = _rng(seed + 2)
+    idx = {}
+    for t in range(n):
+        bt = t // B
+        idx[t] = [sorted({bt} | {b for b in range(bt) if g.random() < 0.5}) for _ in range(h_kv)]
+    return Q, K, V, dO, p, idx
+
+
+def _loss(Q, K, V, dO, G, p, idx):
+    """sum(dO * O) through the forward oracle (attend_token)."""
+    tot = 0.0
+    for t, blocks in idx.items():
+        o, _ = R.attend_token(Q[t], t, K, V, blocks, G, p)
+        tot += float((dO[t] * o).sum())
+    return tot
+
+
+def pin_grad_finite_differences():
+    """Analytic gradients of the sparse attention against central differences
+    of the forward oracle, at 12 random coordinates of each of Q, K, V."""
+    Q, K, V, dO, p, idx = _grad_case()
+    G = Q.shape[1] // K.shape[1]
+    dQ, dK, dV = R.attention_grad(Q, K, V, dO, G, p, idx)
+    g = _rng(40)
+    eps = 1e-5
+    for X, dX in ((Q, dQ), (K, dK), (V, dV)):
+        for _ in range(12):
+            at = tuple(int(g.integers(0, m)) for m in X.shape)
+            old = X[at]
+            X[at] = old + eps
+            lp = _loss(Q, K, V, dO, G, p, idx)
+            X[at] = old - eps
+            lm = _loss(Q, K, V, dO, G, p, idx)
+            X[at] = old
+            fd = (lp - lm) / (2 * eps)
+            if abs(fd - dX[at]) > 1e-7 * (1 + abs(fd)):
+                return False
+    return True
+
+
+def pin_grad_identities():
+    """Exact identities: the key gradients of a group sum to zero (each row of
+    dl/dz sums to zero); the value gradients sum to the group's upstream
+    gradient (each row of P sums to one); values equal along the keys leave
+    dQ and dK at zero; a query that sees one key gets dq = 0."""
+    Q, K, V, dO, p, idx = _grad_case(seed=33)
+    h_kv = K.shape[1]
+    G = Q.shape[1] // h_kv
+    dQ, dK, dV = R.attention_grad(Q, K, V, dO, G, p, idx)
+    for g in range(h_kv):
+        if not np.allclose(dK[:, g].sum(axis=0), 0.0, atol=1e-11):
+            return False
+        want = dO[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+        if not np.allclose(dV[:, g].sum(axis=0), want, atol=1e-11):
+            return False
+    Vc = np.broadcast_to(_rng(34).standard_normal((1, h_kv, K.shape[2])), K.shape).copy()
+    dQc, dKc, _ = R.attention_grad(Q, K, Vc, dO, G, p, idx)
+    if not (np.allclose(dQc, 0.0, atol=1e-12) and np.allclose(dKc, 0.0, atol=1e-12)):
+        return False
+    dq, parts = R.attend_token_grad(Q[0], dO[0], 0, K, V, [[0]] * h_kv, G, p)
+    return bool(np.allclose(dq, 0.0, atol=1e-14) and all(len(u) == 1 for u, _, _ in parts))
+
+
+def pin_grad_dense_torch():
+    """Dense causal gradients against torch autograd of
+    scaled_dot_product_attention in float64 (K, V repeated per group)."""
+    Q, K, V = _tiny(35, n=96, h_q=4, h_kv=2, d=8)
+    dO = _rng(36).standard_normal(Q.shape)
+    G = 2
+    p = R.Params(block_size=16)
+    dQ, dK, dV = R.attention_grad(Q, K, V, dO, G, p, dense=True)
+    q = torch.tensor(Q).permute(1, 0, 2).requires_grad_(True)
+    k = torch.tensor(K).permute(1, 0, 2).requires_grad_(True)
+    v = torch.tensor(V).permute(1, 0, 2).requires_grad_(True)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        q, k.repeat_interleave(G, 0), v.repeat_interleave(G, 0), is_causal=True)
+    o.backward(torch.tensor(dO).permute(1, 0, 2))
+    return (_close(dQ, q.grad.permute(1, 0, 2).numpy(), 1e-11)
+            and _close(dK, k.grad.permute(1, 0, 2).numpy(), 1e-11)
+            and _close(dV, v.grad.permute(1, 0, 2).numpy(), 1e-11))
+
+
 ALL_PINS = [pin_worked_example, pin_stage_parameters, pin_window_counts,
             pin_compress_by_convolution, pin_compress_constant, pin_compress_bf16_rounding,
             pin_lse_exact_scipy, pin_lse_approx_scipy, pin_group_sum_softmax,
             pin_constant_keys, pin_approx_bound, pin_pool_by_token_overlap,
             pin_topk_full_sort, pin_attention_sdpa, pin_attention_special_cases,
-            pin_cost_identities]
+            pin_cost_identities, pin_grad_finite_differences, pin_grad_identities,
+            pin_grad_dense_torch]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -433,6 +521,46 @@ def _wrong_select(t, score_row, p):                          # ties toward the h
     return blocks, {}
 
 
+def _wrong_attend_grad_no_delta(q, dout, K, V, keys_per_group, G, scale):   # drops the dO . o term
+    q, dout = R.as_f64(q), R.as_f64(dout)
+    h_q, d = q.shape
+    dq = np.zeros((h_q, d))
+    dk = [np.zeros((len(u), d)) for u in keys_per_group]
+    dv = [np.zeros((len(u), d)) for u in keys_per_group]
+    for h in range(h_q):
+        g = h // G
+        u = keys_per_group[g]
+        z = scale * (K[u, g] @ q[h])
+        P = np.exp(z - z.max())
+        P /= P.sum()
+        dz = P * (V[u, g] @ dout[h])
+        dq[h] = scale * (dz @ K[u, g])
+        dk[g] += scale * np.outer(dz, q[h])
+        dv[g] += np.outer(P, dout[h])
+    return dq, dk, dv
+
+
+def _wrong_attend_grad_unscaled_dk(q, dout, K, V, keys_per_group, G, scale):  # dk without the scale
+    dq, dk, dv = _ORIG_ATTEND_GRAD(q, dout, K, V, keys_per_group, G, scale)
+    return dq, [x / scale for x in dk], dv
+
+
+def _wrong_attend_grad_dv_transposed(q, dout, K, V, keys_per_group, G, scale):  # dv from dz, not P
+    q, dout = R.as_f64(q), R.as_f64(dout)
+    dq, dk, dv = _ORIG_ATTEND_GRAD(q, dout, K, V, keys_per_group, G, scale)
+    for h in range(q.shape[0]):
+        g = h // G
+        u = keys_per_group[g]
+        z = scale * (K[u, g] @ q[h])
+        P = np.exp(z - z.max())
+        P /= P.sum()
+        dv[g] += np.outer(P[::-1], dout[h]) - np.outer(P, dout[h])
+    return dq, dk, dv
+
+
+_ORIG_ATTEND_GRAD = R._attend_grad
+
+
 def _params_pad0(**kw):
     kw.setdefault("pool_pad", 0)
     return _ORIG_PARAMS(**kw)
@@ -447,6 +575,9 @@ MUTATIONS = {
     "window_start_shifted": ("compress_keys", _wrong_compress),
     "causal_excludes_self": ("attend_token", _wrong_attend),
     "ties_toward_higher_index": ("select_from_scores", _wrong_select),
+    "grad_without_delta_term": ("_attend_grad", _wrong_attend_grad_no_delta),
+    "grad_dk_unscaled": ("_attend_grad", _wrong_attend_grad_unscaled_dk),
+    "grad_dv_keys_reversed": ("_attend_grad", _wrong_attend_grad_dv_transposed),
 }
 
 
