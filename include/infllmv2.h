@@ -212,6 +212,56 @@ int infllmv2_dense_attn(const void* q, const void* k, const void* v,
                         void* out, float* lse_out,
                         void* workspace, size_t* workspace_bytes, void* stream);
 
+/*
+ * infllmv2_sparse_attn_bwd — gradients of infllmv2_sparse_attn (block_idx
+ * given) or infllmv2_dense_attn (block_idx NULL) with the block sets held
+ * fixed.  The method is trained through its sparse attention (reading notes
+ * "论文阅读：InfLLM-V2", section "训练是怎么做的": long-context fine-tuning
+ * with the plain next-token objective); the top-k selection is piecewise
+ * constant in q and k, so no gradient flows into the scoring path.  With
+ * P[t, h, u] the forward's probabilities over the same key sets T:
+ *
+ *   D[t, h]   = sum_d dout[t, h, d] * out[t, h, d]
+ *   dS[t,h,u] = P[t, h, u] * (dout[t, h] . v[u, g] - D[t, h])
+ *   dq[t, h]  = softmax_scale * sum_u dS[t, h, u] k[u, g]
+ *   dk[u, g]  = softmax_scale * sum_{t, h in g} dS[t, h, u] q[t, h]
+ *   dv[u, g]  = sum_{t, h in g} P[t, h, u] dout[t, h]
+ *
+ * P is recomputed from q, k and the forward's lse (lse_out of the forward
+ * call, natural log).  Block lists are read exactly as the forward reads
+ * them (a set per row; -1, repeats and blocks later than b_t skipped).
+ *
+ *   q, out, dout   bf16 [rows_q, h_q, head_dim]  (out, lse: the forward's)
+ *   lse            float [h_q, rows_q]
+ *   k, v           bf16 [rows_k, h_kv, head_dim]  (v in its natural layout)
+ *   block_idx      int32 [h_kv, rows_q, n_sel], or NULL for dense causal
+ *   dq             bf16 [rows_q, h_q, head_dim]: rows of every sequence written
+ *   dk, dv         bf16 [rows_k, h_kv, head_dim]: rows of every sequence
+ *                  written (zero for keys no query attends)
+ *   workspace      size from a query with the same shape arguments (and the
+ *                  same n_sel / n_init / n_local, or block_idx NULL): per
+ *                  query row and KV group 8 KB (Q and dO re-laid out) plus
+ *                  128 B of statistics; per key row 1 KB (fp32 dk, dv); two
+ *                  16-bit token-mask tables of h_kv * batch * ceil(max_q/16)
+ *                  * ceil(max_k/64) entries; the work list of the key-major
+ *                  pass.
+ *   Supported: head_dim 128, block_size 64, group size 1, 2, 4, 8 or 16, at
+ *   most 8192 blocks per sequence and 65535 tiles of 16 query rows.  dk and
+ *   dv are sums of fp32 atomic additions, so their last bits may differ from
+ *   run to run; dq is deterministic.
+ */
+int infllmv2_sparse_attn_bwd(const void* q, const void* k, const void* v,
+                             const void* out, const float* lse, const void* dout,
+                             const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                             const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                             int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                             int64_t rows_q, int64_t rows_k,
+                             int32_t h_q, int32_t h_kv, int32_t head_dim, int32_t block_size,
+                             const int32_t* block_idx, int32_t n_sel, int32_t n_init,
+                             int32_t n_local, float softmax_scale,
+                             void* dq, void* dk, void* dv,
+                             void* workspace, size_t* workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -175,3 +175,51 @@ def test_no_workspace_is_not_a_size_query(lib):
                                  8192, 32, 2, 128, 0.088, 8192, None, None, None, None, None)
     assert rc == EINVAL
     assert B._ws(None) == (None, None)
+
+
+def _bwd(lib, **kw):
+    a = dict(batch=1, max_q=4096, max_k=4096, rows_q=4096, rows_k=4096, h_q=32, h_kv=2, d=128,
+             B=64, idx=None, n_sel=0, n_init=0, n_local=0, scale=0.088)
+    a.update(kw)
+    size = ctypes.c_size_t(0)
+    rc = lib.infllmv2_sparse_attn_bwd(
+        None, None, None, None, None, None, None, None, None, None, a["batch"], a["max_q"],
+        a["max_k"], a["rows_q"], a["rows_k"], a["h_q"], a["h_kv"], a["d"], a["B"], a["idx"],
+        a["n_sel"], a["n_init"], a["n_local"], a["scale"], None, None, None, None,
+        ctypes.byref(size), None)
+    return rc, size.value
+
+
+def test_backward_workspace_layout(lib):
+    """Workspace of the backward: statistics (2 x 64 B) and the re-laid-out
+    Q, dO (2 x 4 KB) per (query row, group); fp32 dk, dv per (key row, group);
+    two 16-bit mask tables; per-block item counts; the work list."""
+    rows, n, h_kv = 4096, 4096, 2
+    for dense, n_sel, n_init, n_local in ((True, 0, 0, 0), (False, 63, 1, 32)):
+        rc, size = _bwd(lib, idx=None if dense else ctypes.c_void_p(16), n_sel=n_sel,
+                        n_init=n_init, n_local=n_local)
+        assert rc == OK
+        ntiles, nblk = n // 16, n // 64
+        nb = h_kv * nblk
+        per_row = nblk if dense else min(nblk, n_sel + n_init + n_local)
+        wmax = -(-h_kv * rows * per_row // 1024) + nb + 1
+        want = (2 * align(rows * h_kv * 16 * 4) + 2 * align(rows * h_kv * 128 * 16 * 2)
+                + 2 * align(n * h_kv * 128 * 4) + 2 * align(nb * ntiles * 2) + align(nb * 4)
+                + align(wmax * 8) + align(4))
+        assert size == want, (dense, size, want)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(max_k=64 * 8193, max_q=64, rows_k=64 * 8193), EUNSUP),   # > 8192 blocks
+    (dict(d=64), EUNSUP),
+    (dict(B=32), EUNSUP),
+    (dict(h_q=24, h_kv=2), EUNSUP),         # G = 12
+    (dict(h_q=31), EINVAL),
+    (dict(scale=0.0), EINVAL),
+    (dict(idx=ctypes.c_void_p(16), n_sel=0), EINVAL),
+    (dict(max_q=5000), EINVAL),
+])
+def test_backward_validation(lib, kw, code):
+    rc, _ = _bwd(lib, **kw)
+    assert rc == code
+    assert lib.infllmv2_last_error()

@@ -1,0 +1,218 @@
+"""GPU parity of the attention backward (infllmv2_sparse_attn_bwd) against the
+fp64 oracle's gradients (oracle.reference.attention_grad / attend_token_grad).
+
+The backward recomputes P from the forward's LSE, rounds P and dS to bf16 as
+MFMA operands and D = dO . O uses the forward's bf16 output, with fp32
+accumulation; outputs are rounded to bf16.  Each of these roundings carries a
+relative error of at most 2^-9 on one factor of a sum of many terms with
+mixed signs, so the gradients' relative RMS error stays near 2^-8 and the
+bar is set at 1.5e-2 (relative RMS over a tensor) and 3e-2 x max|ref|
+(max-abs), with the observed values printed.
+
+Block lists are read as sets: the GPU gets scrambled rows with -1 pads,
+repeats and blocks after the query's own; the oracle gets the clean set.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.reference as R
+from trainable_block_sparse_compress_amd import binding as B
+from trainable_block_sparse_compress_amd import datagen as D
+from trainable_block_sparse_compress_amd import pipeline as P
+from tests.gpu_util import i32, say, to_dev, to_f64
+from tests.helpers import sample_positions
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL_RMS = 1.5e-2
+GRAD_MAX_REL = 3e-2
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return B.load()
+
+
+def _starts(lengths):
+    return [int(x) for x in np.concatenate([[0], np.cumsum(lengths)[:-1]])]
+
+
+def grad_errors(gpu, ref):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    err = gpu - ref
+    scale = max(float(np.abs(ref).max()), 1e-30)
+    rms = float(np.sqrt((err ** 2).mean()))
+    ref_rms = max(float(np.sqrt((ref ** 2).mean())), 1e-30)
+    return float(np.abs(err).max()) / scale, rms / ref_rms
+
+
+def _scrambled_lists(lengths, h_kv, p: R.Params, seed, extra=4):
+    """GPU rows (scrambled, with junk) and the oracle's clean per-group sets."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = sum(lengths)
+    n_cols = p.n_topk + extra
+    idx = np.full((h_kv, rows, n_cols), -1, dtype=np.int32)
+    sets = {}
+    st = _starts(lengths)
+    for s, n in enumerate(lengths):
+        for t in range(n):
+            bt = t // 64
+            fixed = set(range(min(p.n_init, bt + 1))) | set(range(max(0, bt - p.n_local + 1), bt + 1))
+            for g in range(h_kv):
+                rest = [b for b in range(bt + 1) if b not in fixed]
+                kk = min(len(rest), p.n_topk)
+                pick = rng.choice(rest, size=kk, replace=False).tolist() if kk else []
+                junk = []
+                if pick:
+                    junk.append(pick[0])                        # a repeat
+                junk += [-1, bt + 1 + int(rng.integers(0, 4))]  # a pad and a future block
+                row = (pick + junk)[:n_cols]
+                rng.shuffle(row)
+                idx[g, st[s] + t, :len(row)] = row
+                sets[(s, t, g)] = sorted(fixed | set(pick))
+    return idx, sets
+
+
+def _run(q, k, v, lengths, idx, p, dense, dout):
+    st = _starts(lengths)
+    h_q, h_kv = q.shape[1], k.shape[1]
+    rows = q.shape[0]
+    n, scale = max(lengths), 1 / math.sqrt(128)
+    args = (i32(st), i32(lengths), i32(st), i32(lengths), len(lengths), n, n)
+    out = torch.empty_like(q)
+    lse = torch.empty((h_q, rows), dtype=torch.float32, device="cuda")
+    n_sel = 0 if dense else idx.shape[-1]
+    ws = torch.empty(max(1, B.attn_workspace(h_q, h_kv, len(lengths), n, n, rows, n_sel=n_sel,
+                                             n_init=p.n_init, n_local=p.n_local)),
+                     dtype=torch.uint8, device="cuda")
+    if dense:
+        B.dense_attn(q, k, v, *args, scale, out, lse, ws)
+    else:
+        B.sparse_attn(q, k, v, *args, idx, p.n_init, p.n_local, scale, out, lse, ws)
+    wsb = torch.empty(B.attn_bwd_workspace(h_q, h_kv, len(lengths), n, n, rows, k.shape[0],
+                                           n_sel=n_sel, n_init=p.n_init, n_local=p.n_local),
+                      dtype=torch.uint8, device="cuda")
+    dq = torch.full_like(q, float("nan"))
+    dk = torch.full_like(k, float("nan"))
+    dv = torch.full_like(v, float("nan"))
+    B.sparse_attn_bwd(q, k, v, out, lse, dout, *args, None if dense else idx, p.n_init, p.n_local,
+                      scale, dq, dk, dv, wsb)
+    torch.cuda.synchronize()
+    return to_f64(dq), to_f64(dk), to_f64(dv)
+
+
+@pytest.mark.parametrize("lengths,h_q,h_kv,sel", [
+    ([700, 1100], 32, 2, (1, 4, 6)),
+    ([1500], 2, 1, (1, 2, 3)),
+    ([37, 900], 16, 2, (0, 0, 8)),
+    ([130, 2000], 8, 8, (2, 3, 9)),
+])
+def test_backward_sparse_given_lists(lib, lengths, h_q, h_kv, sel):
+    say(f"backward sparse lengths={lengths} h_q={h_q} h_kv={h_kv} sel={sel}")
+    p = R.Params(n_init=sel[0], n_local=sel[1], n_topk=sel[2])
+    inp = D.make_prefill(41, lengths, h_q, h_kv)
+    dO = D.make_grad(42, sum(lengths), h_q)
+    idx_np, sets = _scrambled_lists(lengths, h_kv, p, seed=43)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    dq, dk, dv = _run(q, k, v, lengths, torch.from_numpy(idx_np).cuda(), p, False, to_dev(dO))
+    st = _starts(lengths)
+    G = h_q // h_kv
+    for s, n in enumerate(lengths):
+        sl = slice(st[s], st[s] + n)
+        idx_by_pos = {t: [sets[(s, t, g)] for g in range(h_kv)] for t in range(n)}
+        rq, rk, rv = R.attention_grad(inp.q[sl], inp.k[sl], inp.v[sl], dO[sl], G, p, idx_by_pos)
+        for name, got, ref in (("dq", dq[sl], rq), ("dk", dk[sl], rk), ("dv", dv[sl], rv)):
+            mr, rr = grad_errors(got, ref)
+            say(f"  seq {s} {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+            assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (s, name, mr, rr)
+
+
+@pytest.mark.parametrize("lengths,h_q,h_kv", [([300, 1000], 32, 2), ([777], 4, 2)])
+def test_backward_dense(lib, lengths, h_q, h_kv):
+    say(f"backward dense lengths={lengths} h_q={h_q} h_kv={h_kv}")
+    p = R.Params()
+    inp = D.make_prefill(44, lengths, h_q, h_kv)
+    dO = D.make_grad(45, sum(lengths), h_q)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    dq, dk, dv = _run(q, k, v, lengths, None, p, True, to_dev(dO))
+    st = _starts(lengths)
+    for s, n in enumerate(lengths):
+        sl = slice(st[s], st[s] + n)
+        rq, rk, rv = R.attention_grad(inp.q[sl], inp.k[sl], inp.v[sl], dO[sl], h_q // h_kv, p,
+                                      dense=True)
+        for name, got, ref in (("dq", dq[sl], rq), ("dk", dk[sl], rk), ("dv", dv[sl], rv)):
+            mr, rr = grad_errors(got, ref)
+            say(f"  seq {s} {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+            assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (s, name, mr, rr)
+
+
+def _headline_lists(n, h_kv, p: R.Params, seed):
+    """Top-k rows of the 1 + 32 + 63 layout drawn on the host: 63 uniform
+    candidates from [n_init, b_t - n_local] per row (repeats allowed: rows
+    are sets), -1 where a row has no candidate."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bt = np.arange(n) // 64
+    ncand = np.maximum(0, bt - p.n_local - p.n_init + 1)
+    u = rng.random((h_kv, n, p.n_topk))
+    idx = (p.n_init + np.floor(u * ncand[None, :, None])).astype(np.int32)
+    idx[:, ncand == 0, :] = -1
+    return idx
+
+
+@pytest.mark.parametrize("n", [32768, 131072])
+def test_backward_full_size_sampled(lib, n):
+    """Full size (32q/2kv, |I| = 1 + 32 + 63, host-drawn top-k rows): dq at
+    sampled rows and dK / dV of the last two blocks (every row attending them
+    sits in the sequence's tail) against the oracle, and two identities over
+    all keys: per group the dV rows sum to the group's summed dO, and the dK
+    rows sum to zero (each row of dS sums to zero)."""
+    say(f"backward full size n={n}")
+    h_q, h_kv = 32, 2
+    G = h_q // h_kv
+    p = R.Params()
+    inp = D.make_prefill(3, n, h_q, h_kv, n_needles=32)
+    dO = D.make_grad(46, n, h_q)
+    idx_np = _headline_lists(n, h_kv, p, seed=47)
+    q, k, v, dout = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(dO)
+    dq, dk, dv = _run(q, k, v, [n], torch.from_numpy(idx_np).cuda(), p, False, dout)
+    Kf, Vf = R.as_f64(inp.k), R.as_f64(inp.v)
+
+    def blocks_of(t):
+        bt = t // 64
+        fixed = set(range(min(p.n_init, bt + 1))) | set(range(max(0, bt - p.n_local + 1), bt + 1))
+        return [sorted(fixed | {int(b) for b in idx_np[g, t] if 0 <= b <= bt}) for g in range(h_kv)]
+
+    # (rows are compared together: a row with one visible key has dq = 0)
+    rows = sample_positions(n, 24, seed=5)
+    ref = np.stack([R.attend_token_grad(inp.q[t], dO[t], t, Kf, Vf, blocks_of(t), G, p)[0]
+                    for t in rows])
+    mr, rr = grad_errors(dq[rows], ref)
+    say(f"  dq at {len(rows)} sampled rows: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+    assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (mr, rr)
+    b0 = (n - 1) // 64 - 1
+    rk = np.zeros((n - 64 * b0, h_kv, 128))
+    rv = np.zeros((n - 64 * b0, h_kv, 128))
+    for t in range(64 * b0, n):
+        _, parts = R.attend_token_grad(inp.q[t], dO[t], t, Kf, Vf, blocks_of(t), G, p)
+        for g, (u, gk, gv) in enumerate(parts):
+            m = u >= 64 * b0
+            rk[u[m] - 64 * b0, g] += gk[m]
+            rv[u[m] - 64 * b0, g] += gv[m]
+    for name, got, ref in (("dk", dk[64 * b0:], rk), ("dv", dv[64 * b0:], rv)):
+        mr, rr = grad_errors(got, ref)
+        say(f"  tail blocks {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+        assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (name, mr, rr)
+    dOf = R.as_f64(dO)
+    for g in range(h_kv):
+        want = dOf[:, g * G:(g + 1) * G].sum(axis=(0, 1))
+        dv_err = np.abs(dv[:, g].sum(axis=0) - want) / np.abs(dv[:, g]).sum(axis=0)
+        dk_err = np.abs(dk[:, g].sum(axis=0)) / np.abs(dk[:, g]).sum(axis=0)
+        say(f"  group {g}: |sum dv - sum dO| / sum|dv| {dv_err.max():.2e}, "
+            f"|sum dk| / sum|dk| {dk_err.max():.2e}")
+        assert dv_err.max() <= 1e-2 and dk_err.max() <= 1e-2, (g, dv_err.max(), dk_err.max())

@@ -16,6 +16,7 @@ import torch
 __all__ = [
     "InfLLMv2Error", "load", "library_path", "version", "compress_k", "select_blocks",
     "select_blocks_workspace", "sparse_attn", "dense_attn", "attn_workspace",
+    "sparse_attn_bwd", "attn_bwd_workspace",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -38,6 +39,9 @@ _SIGS = {
                              _I32, _I32, _P, _I32, _I32, _I32, _F, _I64, _P, _P, _P, _SZP, _P],
     "infllmv2_dense_attn": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32, _I32,
                             _I32, _F, _I64, _P, _P, _P, _SZP, _P],
+    "infllmv2_sparse_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64,
+                                 _I64, _I32, _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _P, _P,
+                                 _P, _P, _SZP, _P],
 }
 
 
@@ -197,3 +201,36 @@ def dense_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch,
         _i32(seqused_k, "seqused_k"), batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, h_q,
         h_kv, d, softmax_scale, v_seq_stride, _bf16(out, "out"), _ptr(lse), ws, ws_bytes,
         _stream()))
+
+
+def attn_bwd_workspace(h_q, h_kv, batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, n_sel=0,
+                       n_init=0, n_local=0) -> int:
+    """Workspace bytes of sparse_attn_bwd for these sizes (n_sel == 0: the
+    dense backward)."""
+    size = ctypes.c_size_t(0)
+    _check(load().infllmv2_sparse_attn_bwd(
+        None, None, None, None, None, None, None, None, None, None, batch, max_seqlen_q,
+        max_seqlen_k, rows_q, rows_k, h_q, h_kv, 128, 64, _P(1) if n_sel > 0 else None, n_sel,
+        n_init, n_local, 1.0, None, None, None, None, ctypes.byref(size), None))
+    return size.value
+
+
+def sparse_attn_bwd(q, k, v, out, lse, dout, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k,
+                    batch, max_seqlen_q, max_seqlen_k, block_idx, n_init, n_local, softmax_scale,
+                    dq, dk, dv, workspace, block_size=64):
+    """Gradients dq, dk, dv (bf16, written in place) of the sparse attention
+    (block_idx given) or the dense causal attention (block_idx None), from the
+    forward's out and lse and the upstream gradient dout."""
+    rows_q, h_q, d = q.shape
+    rows_k, h_kv, _ = k.shape
+    n_sel = block_idx.shape[-1] if block_idx is not None else 0
+    if lse is None or lse.dtype != torch.float32:
+        raise InfLLMv2Error("lse must be the forward's float32 [h_q, rows_q] LSE")
+    ws, ws_bytes = _ws(workspace)
+    _check(load().infllmv2_sparse_attn_bwd(
+        _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(out, "out"), _ptr(lse),
+        _bf16(dout, "dout"), _i32(cu_seqlens_q, "cu_seqlens_q"), _i32(seqused_q, "seqused_q"),
+        _i32(cu_seqlens_k, "cu_seqlens_k"), _i32(seqused_k, "seqused_k"), batch, max_seqlen_q,
+        max_seqlen_k, rows_q, rows_k, h_q, h_kv, d, block_size, _i32(block_idx, "block_idx"),
+        n_sel, n_init, n_local, softmax_scale, _bf16(dq, "dq"), _bf16(dk, "dk"), _bf16(dv, "dv"),
+        ws, ws_bytes, _stream()))

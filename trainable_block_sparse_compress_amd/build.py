@@ -31,9 +31,16 @@ CFLAGS = [
 ]
 
 
+# Per-file flags.  backward.hip: its key-major kernel keeps a 64 x 128 fp32
+# dK and dV (256 registers) besides its operands; with MFMA results in
+# VGPRs the allocator parks the overflow in AGPRs instead of spilling to
+# scratch memory.
+FILE_FLAGS = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in line)

@@ -222,6 +222,41 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_s
   return ok();
 }
 
+// Workspace of the backward: offsets of its buffers.
+struct BwdLayout {
+  int64_t ntiles, nblk, wmax;
+  size_t lse2, dd, qt, dot, dk_acc, dv_acc, mask_t, mask_b, items, work, nwork, total;
+};
+BwdLayout bwd_layout(int64_t rows_q, int64_t rows_k, int batch, int max_seqlen_q, int max_seqlen_k,
+                     int h_kv, bool dense, int n_sel, int n_init, int n_local) {
+  BwdLayout L;
+  L.ntiles = std::max<int64_t>(1, ceil_div(max_seqlen_q, 16));
+  L.nblk = std::max<int64_t>(1, ceil_div(max_seqlen_k, kBlock));
+  const int64_t per_row = dense ? L.nblk : std::min<int64_t>(L.nblk, (int64_t)n_sel + n_init + n_local);
+  // Every work item but the last of a block holds kBwdChunk tokens.
+  const int64_t nb = (int64_t)h_kv * batch * L.nblk;
+  L.wmax = ceil_div((int64_t)h_kv * rows_q * per_row, kBwdChunk) + nb + 1;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L.lse2 = take((size_t)rows_q * h_kv * 16 * sizeof(float));
+  L.dd = take((size_t)rows_q * h_kv * 16 * sizeof(float));
+  L.qt = take((size_t)rows_q * h_kv * kHeadDim * 16 * 2);
+  L.dot = take((size_t)rows_q * h_kv * kHeadDim * 16 * 2);
+  L.dk_acc = take((size_t)rows_k * h_kv * kHeadDim * sizeof(float));
+  L.dv_acc = take((size_t)rows_k * h_kv * kHeadDim * sizeof(float));
+  L.mask_t = take((size_t)nb * L.ntiles * 2);
+  L.mask_b = take((size_t)nb * L.ntiles * 2);
+  L.items = take((size_t)nb * sizeof(int32_t));
+  L.work = take((size_t)L.wmax * 2 * sizeof(int32_t));
+  L.nwork = take(sizeof(int32_t));
+  L.total = off;
+  return L;
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,3 +455,90 @@ int infllmv2_dense_attn(const void* q, const void* k, const void* v, const int32
 }
 
 }  // extern "C"
+
+extern "C" int infllmv2_sparse_attn_bwd(const void* q, const void* k, const void* v, const void* out,
+                                        const float* lse, const void* dout,
+                                        const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                                        const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                                        int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                        int64_t rows_q, int64_t rows_k, int32_t h_q, int32_t h_kv,
+                                        int32_t head_dim, int32_t block_size,
+                                        const int32_t* block_idx, int32_t n_sel, int32_t n_init,
+                                        int32_t n_local, float softmax_scale, void* dq, void* dk,
+                                        void* dv, void* workspace, size_t* workspace_bytes,
+                                        void* stream) {
+  const bool dense = block_idx == nullptr;
+  int rc = common_seq_checks(batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k);
+  if (rc) return rc;
+  REQUIRE(head_dim == kHeadDim, INFLLMV2_EUNSUPPORTED, "head_dim %d unsupported (128 only)", head_dim);
+  REQUIRE(block_size == kBlock, INFLLMV2_EUNSUPPORTED, "block_size %d unsupported (64 only)", block_size);
+  REQUIRE(h_kv >= 1 && h_q >= 1 && h_q % h_kv == 0, INFLLMV2_EINVAL, "h_q %d not a multiple of h_kv %d", h_q, h_kv);
+  REQUIRE(h_kv <= kMaxGrid, INFLLMV2_EINVAL, "h_kv too large");
+  REQUIRE(group_ok(h_q / h_kv), INFLLMV2_EUNSUPPORTED, "group size %d unsupported (1, 2, 4, 8, 16)", h_q / h_kv);
+  REQUIRE(std::isfinite(softmax_scale) && softmax_scale > 0.f, INFLLMV2_EINVAL, "softmax_scale must be finite and > 0");
+  if (!dense) {
+    REQUIRE(n_sel >= 1, INFLLMV2_EINVAL, "n_sel must be >= 1");
+    REQUIRE(n_init >= 0 && n_local >= 0, INFLLMV2_EINVAL, "n_init and n_local must be >= 0");
+  }
+  REQUIRE(ceil_div(max_seqlen_k, kBlock) <= kBwdMaxBlocks, INFLLMV2_EUNSUPPORTED,
+          "more than %d blocks per sequence", kBwdMaxBlocks);
+  REQUIRE(ceil_div(max_seqlen_q, 16) <= kMaxGrid, INFLLMV2_EUNSUPPORTED, "too many query rows per sequence");
+  REQUIRE((int64_t)h_kv * batch <= kMaxGrid, INFLLMV2_EUNSUPPORTED, "h_kv * batch above %d", kMaxGrid);
+  REQUIRE(ceil_div(rows_q, 4) <= 0x7FFFFFFF, INFLLMV2_EUNSUPPORTED, "too many query rows");
+  const BwdLayout L = bwd_layout(rows_q, rows_k, batch, max_seqlen_q, max_seqlen_k, h_kv, dense,
+                                 n_sel, n_init, n_local);
+  REQUIRE(L.wmax <= 0x7FFFFFFF, INFLLMV2_EUNSUPPORTED, "too many work items");
+  bool query = false;
+  rc = workspace_check(workspace, workspace_bytes, L.total, &query);
+  if (rc || query) return rc;
+  if (batch == 0 || max_seqlen_q == 0) return ok();
+  REQUIRE(rows_q >= 1 && rows_k >= 1, INFLLMV2_EINVAL, "rows_q and rows_k must be >= 1");
+  REQUIRE(q && k && v && out && lse && dout && dq && dk && dv && cu_seqlens_q && cu_seqlens_k,
+          INFLLMV2_EINVAL, "null pointer");
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  BwdArgs a;
+  a.q = reinterpret_cast<const uint16_t*>(q);
+  a.k = reinterpret_cast<const uint16_t*>(k);
+  a.v = reinterpret_cast<const uint16_t*>(v);
+  a.out = reinterpret_cast<const uint16_t*>(out);
+  a.lse = lse;
+  a.dout = reinterpret_cast<const uint16_t*>(dout);
+  a.cu_q = cu_seqlens_q;
+  a.used_q = seqused_q;
+  a.cu_k = cu_seqlens_k;
+  a.used_k = seqused_k;
+  a.rows_q = rows_q;
+  a.rows_k = rows_k;
+  a.batch = batch;
+  a.h_q = h_q;
+  a.h_kv = h_kv;
+  a.G = h_q / h_kv;
+  a.bidx = dense ? nullptr : block_idx;
+  a.n_sel = dense ? 0 : n_sel;
+  a.n_init = dense ? 0 : n_init;
+  a.n_local = dense ? 0 : n_local;
+  a.scale = softmax_scale;
+  a.c = softmax_scale * 1.4426950408889634f;
+  a.dq = reinterpret_cast<uint16_t*>(dq);
+  a.dk = reinterpret_cast<uint16_t*>(dk);
+  a.dv = reinterpret_cast<uint16_t*>(dv);
+  a.lse2 = reinterpret_cast<float*>(ws + L.lse2);
+  a.dd = reinterpret_cast<float*>(ws + L.dd);
+  a.qt = reinterpret_cast<uint16_t*>(ws + L.qt);
+  a.dot = reinterpret_cast<uint16_t*>(ws + L.dot);
+  a.dk_acc = reinterpret_cast<float*>(ws + L.dk_acc);
+  a.dv_acc = reinterpret_cast<float*>(ws + L.dv_acc);
+  a.mask_t = reinterpret_cast<uint16_t*>(ws + L.mask_t);
+  a.mask_b = reinterpret_cast<uint16_t*>(ws + L.mask_b);
+  a.ntiles = (int)L.ntiles;
+  a.nblk = (int)L.nblk;
+  a.items = reinterpret_cast<int32_t*>(ws + L.items);
+  a.work = reinterpret_cast<int32_t*>(ws + L.work);
+  a.nwork = reinterpret_cast<int32_t*>(ws + L.nwork);
+  a.wmax = (int)L.wmax;
+  rc = hip_status(launch_attention_bwd(a, max_seqlen_q, max_seqlen_k, reinterpret_cast<hipStream_t>(stream)),
+                  "attention backward launch");
+  if (rc) return rc;
+  return ok();
+}

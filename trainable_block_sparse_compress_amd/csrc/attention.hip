@@ -26,18 +26,11 @@
 // so P never leaves registers, and V^T fragments are 8 consecutive keys of one
 // dim: one 16-byte load.
 #include "kernels.hpp"
+#include "tile_common.hpp"
 
 namespace infllmv2 {
 
 namespace {
-
-// Key held by row r of S^T key tile kt (a 64-key block has 4 tiles of 16).
-__device__ __forceinline__ int key_of(int kt, int r) {
-  return 32 * (kt >> 1) + 8 * (r >> 2) + 4 * (kt & 1) + (r & 3);
-}
-// LDS swizzle of K rows: the 8 rows a group of 8 lanes reads together map to
-// distinct 16-byte bank groups.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row >> 1) & 4); }
 
 // Zero the bf16 lanes of an 8-key V^T fragment whose key (first + i) >= limit.
 __device__ __forceinline__ u32x4 clip_keys(u32x4 v, int first, int limit) {
@@ -47,26 +40,6 @@ __device__ __forceinline__ u32x4 clip_keys(u32x4 v, int first, int limit) {
     if (first + 2 * i + 1 >= limit) v[i] &= 0x0000FFFFu;
   }
   return v;
-}
-
-// Opaque copy of a lane value: keeps the compiler from folding lane-constant
-// address offsets into per-load invariants hoisted out of the block loops
-// (which would pin dozens of 64-bit addresses in registers).
-__device__ __forceinline__ int opaque(int v) {
-  int r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
-  return r;
-}
-
-__device__ __forceinline__ int64_t opaque64(int64_t v) {
-  const int lo = opaque((int)v), hi = opaque((int)(v >> 32));
-  return (int64_t)(((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo);
-}
-
-// s_waitcnt immediate: wait until at most n vector-memory loads are
-// outstanding (vmcnt in bits 3:0 and 15:14), no wait on expcnt / lgkmcnt.
-__host__ __device__ constexpr int vmcnt_imm(int n) {
-  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
 // Lazy rescaling threshold: the running max is only raised when a block's

@@ -108,4 +108,46 @@ constexpr int kPartFloats = 16 * kHeadDim + 16 + 16;   // O[16][128], l[16], m[1
 hipError_t launch_attention_split(const AttnArgs& a, int64_t rows_q, int splits, float* part,
                                   hipStream_t st);
 
+// Backward of the attention (block sets held fixed).  Operands, outputs and
+// the workspace buffers of the passes (see backward.hip).
+constexpr int kBwdChunk = 1024;        // tokens per key-major work item
+constexpr int kBwdMaxBlocks = 8192;    // blocks per sequence (LDS mask of the mask pass)
+
+struct BwdArgs {
+  const uint16_t* q;        // [rows_q, h_q, 128]
+  const uint16_t* k;        // [rows_k, h_kv, 128]
+  const uint16_t* v;        // [rows_k, h_kv, 128]
+  const uint16_t* out;      // [rows_q, h_q, 128] forward output
+  const float* lse;         // [h_q, rows_q] forward LSE (natural log)
+  const uint16_t* dout;     // [rows_q, h_q, 128] upstream gradient
+  const int32_t* cu_q;
+  const int32_t* used_q;
+  const int32_t* cu_k;
+  const int32_t* used_k;
+  int64_t rows_q, rows_k;
+  int batch, h_q, h_kv, G;
+  const int32_t* bidx;      // [h_kv, rows_q, n_sel] or nullptr (dense)
+  int n_sel, n_init, n_local;
+  float scale, c;           // c = scale * log2(e)
+  uint16_t* dq;             // [rows_q, h_q, 128]
+  uint16_t* dk;             // [rows_k, h_kv, 128]
+  uint16_t* dv;
+  // workspace
+  float* lse2;              // [rows_q, h_kv, 16] LSE * log2(e) per padded head (+inf: no keys / pad)
+  float* dd;                // [rows_q, h_kv, 16] D = dO . O per padded head
+  uint16_t* qt;             // [rows_q, h_kv, 128, 16] Q as [dim][head] per (row, group)
+  uint16_t* dot;            // [rows_q, h_kv, 128, 16] dO likewise
+  float* dk_acc;            // [rows_k, h_kv, 128]
+  float* dv_acc;
+  uint16_t* mask_t;         // [h_kv, batch, ntiles, nblk] tokens of a 16-row tile per block
+  uint16_t* mask_b;         // [h_kv, batch, nblk, ntiles] the same, block-major
+  int ntiles, nblk;         // per-sequence maxima: ceil(max_q / 16), ceil(max_k / 64)
+  int32_t* items;           // [h_kv, batch, nblk] work items per block
+  int32_t* work;            // [wmax, 2] (block index, item within the block)
+  int32_t* nwork;           // number of work items
+  int wmax;
+};
+
+hipError_t launch_attention_bwd(const BwdArgs& a, int max_seqlen_q, int max_seqlen_k, hipStream_t st);
+
 }  // namespace infllmv2

@@ -33,6 +33,7 @@ __all__ = [
     "varlen_lengths",
     "DecodeInputs",
     "make_decode",
+    "make_grad",
 ]
 
 
@@ -194,3 +195,10 @@ def make_decode(seed: int, batch: int, len0: int, steps: int, h_q: int, h_kv: in
     return DecodeInputs(k_cache=k_cache, v_cache=v_cache, q_steps=q_steps, k_steps=k_steps,
                         v_steps=v_steps, len0=len0, needles=needles, seed=seed,
                         needle_scale=needle_scale if n_needles else 0.0)
+
+
+def make_grad(seed: int, rows: int, h_q: int, d: int = 128) -> np.ndarray:
+    """Upstream gradient of the attention output for the backward: i.i.d.
+    N(0, 1) bf16 bits [rows, h_q, d] from its own seeded stream."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _draw_bf16(rng, (int(rows), h_q, d))
