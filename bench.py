@@ -129,12 +129,14 @@ def main():
                          "kernel of known size, to calibrate HBM byte counters)")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="also time the dense causal kernel at the same length (context)")
-    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep"],
+    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep", "backward"],
                     default="prefill",
                     help="prefill (default): one 128K sequence; decode: 16 sequences x 128K "
                          "cache, one token each per step; varlen: 65536 packed tokens of mixed "
                          "lengths through the dense/sparse switch; sweep: the prefill at several "
-                         "selection sizes |I| against the dense kernel at the same length")
+                         "selection sizes |I| against the dense kernel at the same length; "
+                         "backward: the gradients of the 128K sparse attention (selection "
+                         "held fixed)")
     ap.add_argument("--sel", type=str, default="16,32,64,96",
                     help="sweep: selection sizes |I| (1 init block, |I|//3 local, rest top-k)")
     args = ap.parse_args()
@@ -149,6 +151,8 @@ def main():
         return bench_varlen(args)
     if args.workload == "sweep":
         return bench_sweep(args)
+    if args.workload == "backward":
+        return bench_backward(args)
 
     import torch
 
@@ -531,6 +535,75 @@ def bench_sweep(args):
                      "achieved": head["attn_tflops"], "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": head["attn_tflops"] / PEAK_BF16_TFLOPS,
                      "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_backward(args):
+    """Backward of the sparse attention at n = 131072 (32q/2kv, |I| = 96):
+    the block lists come from select_blocks and the forward's output and LSE
+    from sparse_attn, both outside the timed region; one step is one
+    infllmv2_sparse_attn_bwd call (dq, dk, dv from a seeded upstream
+    gradient).  Algorithmic flops: five products of 2*d per (row, head,
+    visible key): S, dP, dV, dK, dQ (the dQ pass recomputing S and dP is not
+    counted)."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    n, h_q, h_kv, d = args.seq, 32, 2, 128
+    print(f"[bench] backward inputs n={n}", file=sys.stderr, flush=True)
+    inp = D.make_prefill(3, n, h_q, h_kv, d, n_needles=32)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    dout = dev(D.make_grad(46, n, h_q, d))
+    vt = v.permute(1, 2, 0).contiguous().view(h_kv, d, 1, n)
+    cfg = P.SparseConfig(lse_mode=args.lse)
+    plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
+    plan.compress(k)
+    plan.select(q)
+    out = torch.empty_like(q)
+    lse = torch.empty((h_q, n), dtype=torch.float32, device="cuda")
+    B.sparse_attn(q, k, vt, plan.cu_q, plan.used_q, plan.cu_k, plan.used_k, 1, n, n,
+                  plan.block_idx, cfg.n_init, cfg.n_local, cfg.scale(d), out, lse, None,
+                  v_seq_stride=n)
+    ws = torch.empty(B.attn_bwd_workspace(h_q, h_kv, 1, n, n, n, n, n_sel=plan.block_idx.shape[-1],
+                                          n_init=cfg.n_init, n_local=cfg.n_local),
+                     dtype=torch.uint8, device="cuda")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+    step = lambda: B.sparse_attn_bwd(q, k, v, out, lse, dout, plan.cu_q, plan.used_q, plan.cu_k,
+                                     plan.used_k, 1, n, n, plan.block_idx, cfg.n_init,
+                                     cfg.n_local, cfg.scale(d), dq, dk, dv, ws)
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    flops = 2.5 * algorithmic_work(n, h_q, h_kv, d)["attn_flops"]
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": "sparse-attn backward tokens/s @128K (32q/2kv, d128, |I|=96; dq, dk, dv)",
+        "value": n / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 Q/K/V (32 needle blocks) and upstream "
+                "gradient",
+        "config": {"workload": f"sparse attention backward, one layer, n={n}", "seq_len": n,
+                   "h_q": h_q, "h_kv": h_kv, "head_dim": d, "n_init": cfg.n_init,
+                   "n_local": cfg.n_local, "n_topk": cfg.n_topk},
+        "roofline": {"bound": "mfma", "kernel": "whole backward (infllmv2_sparse_attn_bwd)",
+                     "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None},
     }
     print(json.dumps(res), flush=True)
 

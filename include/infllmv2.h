@@ -241,14 +241,17 @@ int infllmv2_dense_attn(const void* q, const void* k, const void* v,
  *   workspace      size from a query with the same shape arguments (and the
  *                  same n_sel / n_init / n_local, or block_idx NULL): per
  *                  query row and KV group 8 KB (Q and dO re-laid out) plus
- *                  128 B of statistics; per key row 1 KB (fp32 dk, dv); two
- *                  16-bit token-mask tables of h_kv * batch * ceil(max_q/16)
- *                  * ceil(max_k/64) entries; the work list of the key-major
- *                  pass.
+ *                  128 B of statistics; two 16-bit token-mask tables of
+ *                  h_kv * batch * ceil(max_q/16) * ceil(max_k/64) entries;
+ *                  64 KB of fp32 dK / dV partial sums per work item, where
+ *                  every (KV group, block) with attending rows has
+ *                  ceil(rows / 1024) items (bounded on the host by
+ *                  h_kv * rows_q * min(n_sel + n_init + n_local, blocks) /
+ *                  1024 + h_kv * batch * blocks + 1; about 1.9 GB for one
+ *                  131072-token sequence at |I| = 96).
  *   Supported: head_dim 128, block_size 64, group size 1, 2, 4, 8 or 16, at
- *   most 8192 blocks per sequence and 65535 tiles of 16 query rows.  dk and
- *   dv are sums of fp32 atomic additions, so their last bits may differ from
- *   run to run; dq is deterministic.
+ *   most 8192 blocks per sequence and 65535 tiles of 16 query rows.  The
+ *   results are deterministic (fixed summation order).
  */
 int infllmv2_sparse_attn_bwd(const void* q, const void* k, const void* v,
                              const void* out, const float* lse, const void* dout,

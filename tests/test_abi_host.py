@@ -192,8 +192,9 @@ def _bwd(lib, **kw):
 
 def test_backward_workspace_layout(lib):
     """Workspace of the backward: statistics (2 x 64 B) and the re-laid-out
-    Q, dO (2 x 4 KB) per (query row, group); fp32 dk, dv per (key row, group);
-    two 16-bit mask tables; per-block item counts; the work list."""
+    Q, dO (2 x 4 KB) per (query row, group); 64 KB of fp32 dK / dV partial
+    sums per work item; two 16-bit mask tables; per-block item counts and
+    offsets; the work list."""
     rows, n, h_kv = 4096, 4096, 2
     for dense, n_sel, n_init, n_local in ((True, 0, 0, 0), (False, 63, 1, 32)):
         rc, size = _bwd(lib, idx=None if dense else ctypes.c_void_p(16), n_sel=n_sel,
@@ -204,7 +205,7 @@ def test_backward_workspace_layout(lib):
         per_row = nblk if dense else min(nblk, n_sel + n_init + n_local)
         wmax = -(-h_kv * rows * per_row // 1024) + nb + 1
         want = (2 * align(rows * h_kv * 16 * 4) + 2 * align(rows * h_kv * 128 * 16 * 2)
-                + 2 * align(n * h_kv * 128 * 4) + 2 * align(nb * ntiles * 2) + align(nb * 4)
+                + align(wmax * 16384 * 4) + 2 * align(nb * ntiles * 2) + 2 * align(nb * 4)
                 + align(wmax * 8) + align(4))
         assert size == want, (dense, size, want)
 

@@ -225,7 +225,7 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_s
 // Workspace of the backward: offsets of its buffers.
 struct BwdLayout {
   int64_t ntiles, nblk, wmax;
-  size_t lse2, dd, qt, dot, dk_acc, dv_acc, mask_t, mask_b, items, work, nwork, total;
+  size_t lse2, dd, qt, dot, part, mask_t, mask_b, items, item_off, work, nwork, total;
 };
 BwdLayout bwd_layout(int64_t rows_q, int64_t rows_k, int batch, int max_seqlen_q, int max_seqlen_k,
                      int h_kv, bool dense, int n_sel, int n_init, int n_local) {
@@ -246,11 +246,11 @@ BwdLayout bwd_layout(int64_t rows_q, int64_t rows_k, int batch, int max_seqlen_q
   L.dd = take((size_t)rows_q * h_kv * 16 * sizeof(float));
   L.qt = take((size_t)rows_q * h_kv * kHeadDim * 16 * 2);
   L.dot = take((size_t)rows_q * h_kv * kHeadDim * 16 * 2);
-  L.dk_acc = take((size_t)rows_k * h_kv * kHeadDim * sizeof(float));
-  L.dv_acc = take((size_t)rows_k * h_kv * kHeadDim * sizeof(float));
+  L.part = take((size_t)L.wmax * 16384 * sizeof(float));
   L.mask_t = take((size_t)nb * L.ntiles * 2);
   L.mask_b = take((size_t)nb * L.ntiles * 2);
   L.items = take((size_t)nb * sizeof(int32_t));
+  L.item_off = take((size_t)nb * sizeof(int32_t));
   L.work = take((size_t)L.wmax * 2 * sizeof(int32_t));
   L.nwork = take(sizeof(int32_t));
   L.total = off;
@@ -484,6 +484,8 @@ extern "C" int infllmv2_sparse_attn_bwd(const void* q, const void* k, const void
           "more than %d blocks per sequence", kBwdMaxBlocks);
   REQUIRE(ceil_div(max_seqlen_q, 16) <= kMaxGrid, INFLLMV2_EUNSUPPORTED, "too many query rows per sequence");
   REQUIRE((int64_t)h_kv * batch <= kMaxGrid, INFLLMV2_EUNSUPPORTED, "h_kv * batch above %d", kMaxGrid);
+  REQUIRE((int64_t)h_kv * batch * ceil_div(std::max(1, max_seqlen_k), kBlock) <= 0x7FFFFFFF,
+          INFLLMV2_EUNSUPPORTED, "too many blocks");
   REQUIRE(ceil_div(rows_q, 4) <= 0x7FFFFFFF, INFLLMV2_EUNSUPPORTED, "too many query rows");
   const BwdLayout L = bwd_layout(rows_q, rows_k, batch, max_seqlen_q, max_seqlen_k, h_kv, dense,
                                  n_sel, n_init, n_local);
@@ -527,13 +529,13 @@ extern "C" int infllmv2_sparse_attn_bwd(const void* q, const void* k, const void
   a.dd = reinterpret_cast<float*>(ws + L.dd);
   a.qt = reinterpret_cast<uint16_t*>(ws + L.qt);
   a.dot = reinterpret_cast<uint16_t*>(ws + L.dot);
-  a.dk_acc = reinterpret_cast<float*>(ws + L.dk_acc);
-  a.dv_acc = reinterpret_cast<float*>(ws + L.dv_acc);
+  a.part = reinterpret_cast<float*>(ws + L.part);
   a.mask_t = reinterpret_cast<uint16_t*>(ws + L.mask_t);
   a.mask_b = reinterpret_cast<uint16_t*>(ws + L.mask_b);
   a.ntiles = (int)L.ntiles;
   a.nblk = (int)L.nblk;
   a.items = reinterpret_cast<int32_t*>(ws + L.items);
+  a.item_off = reinterpret_cast<int32_t*>(ws + L.item_off);
   a.work = reinterpret_cast<int32_t*>(ws + L.work);
   a.nwork = reinterpret_cast<int32_t*>(ws + L.nwork);
   a.wmax = (int)L.wmax;

@@ -18,11 +18,13 @@
 //     read as a set; dense: every causal block), transposed block-major;
 //     token counts per block split into work items of at most kBwdChunk
 //     tokens;
-//  3. dK / dV, key-major: one wave per work item holds its K / V block in
-//     registers, streams the item's tokens (ascending) and adds its partial
-//     sums to fp32 accumulators; dQ, query-major: the forward's tile layout,
-//     each block a tile's tokens attend staged once in LDS;
-//  4. the fp32 key gradients are rounded to bf16.
+//  3. dK / dV, key-major: one wave per work item stages its K / V block in
+//     LDS, streams the item's tokens (ascending, the next token's operands in
+//     flight while the current one computes) and stores its fp32 partial
+//     sums; dQ, query-major: the forward's tile layout, each block a tile's
+//     tokens attend staged once in LDS;
+//  4. each block's partial sums are added in item order (deterministic) and
+//     rounded to bf16.
 #include <algorithm>
 #include <type_traits>
 
@@ -96,27 +98,24 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdArgs a) {
   }
   __syncthreads();
   if (!valid) return;
-  // Lane l writes dims 2l and 2l+1, each 16 heads (32 bytes), of Q^T and dO^T.
+  // Lane l = 16*q4 + c16 writes the 32 values its MFMA operand lane reads
+  // in pass 3: dims 16*dt + c16 (dt = 0..7) of heads 4*q4 .. 4*q4+3.
+  const int c16 = lane & 15, q4 = lane >> 4;
 #pragma unroll
   for (int which = 0; which < 2; ++which) {
-    uint32_t w0[8], w1[8];
+    uint32_t w[16];
 #pragma unroll
-    for (int hh = 0; hh < 16; hh += 2) {
-      const uint32_t x = *reinterpret_cast<const uint32_t*>(&tile[wave][which][hh * kHeadDim + 2 * lane]);
-      const uint32_t y = *reinterpret_cast<const uint32_t*>(&tile[wave][which][(hh + 1) * kHeadDim + 2 * lane]);
-      w0[hh / 2] = (x & 0xFFFFu) | (y << 16);
-      w1[hh / 2] = (x >> 16) | (y & 0xFFFF0000u);
-    }
-    uint16_t* dst = (which ? a.dot : a.qt) + ((r * a.h_kv + g) * kHeadDim + 2 * lane) * 16;
-    stg16(dst, u32x4{w0[0], w0[1], w0[2], w0[3]});
-    stg16(dst + 8, u32x4{w0[4], w0[5], w0[6], w0[7]});
-    stg16(dst + 16, u32x4{w1[0], w1[1], w1[2], w1[3]});
-    stg16(dst + 24, u32x4{w1[4], w1[5], w1[6], w1[7]});
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int hp = 0; hp < 2; ++hp) {
+        const uint32_t lo = tile[wave][which][(4 * q4 + 2 * hp) * kHeadDim + 16 * dt + c16];
+        const uint32_t hi = tile[wave][which][(4 * q4 + 2 * hp + 1) * kHeadDim + 16 * dt + c16];
+        w[2 * dt + hp] = lo | (hi << 16);
+      }
+    uint16_t* dst = (which ? a.dot : a.qt) + (r * a.h_kv + g) * 2048 + (c16 * 4 + q4) * 32;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) stg16(dst + 8 * m, u32x4{w[4 * m], w[4 * m + 1], w[4 * m + 2], w[4 * m + 3]});
   }
-}
-
-__global__ __launch_bounds__(256) void bwd_zero_kernel(float* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
 // ---------------------------------------------------------------------------
@@ -214,6 +213,7 @@ __global__ __launch_bounds__(1024) void bwd_list_kernel(BwdArgs a) {
       __syncthreads();
     }
     const int64_t excl = run + sc[tid] - c;
+    if (i < n) a.item_off[i] = (int32_t)(excl < a.wmax ? excl : a.wmax);
     for (int j = 0; j < c; ++j) {
       if (excl + j < a.wmax) {
         a.work[2 * (excl + j)] = (int32_t)i;
@@ -235,10 +235,20 @@ __global__ __launch_bounds__(1024) void bwd_list_kernel(BwdArgs a) {
 //   dV += P^T dO,  dK += dS^T Q   (16 keys x 16 dims, contraction over heads)
 // S and dP come out with lane (c16 = key, q4 -> heads 4*q4 .. +3), exactly
 // the A layout of the head-contracting 16x16x16 products, whose B operands
-// are the [dim][head] copies of Q and dO written by pass 1.
+// are the lane-ordered copies of Q and dO written by pass 1.  The item's
+// tokens are listed in LDS first; the loop then keeps the next token's
+// operands in flight while the current one computes.  The partial sums go
+// to the item's own slot of the workspace (no atomics).
 // ---------------------------------------------------------------------------
+struct TokOps {
+  u32x4 qa[4], da[4];       // Q, dO rows as A operands (dims 32ks + 8q4 .. +7 of head c16)
+  floatx4 l2, dd;           // LSE * log2(e) and D of heads 4q4 .. +3
+};
+
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t kv[2][64 * 256];
+  __shared__ int32_t toks[kBwdChunk];
   const int item = blockIdx.x;
   if (item >= *a.nwork) return;
   const int e = a.work[2 * item], chunk = a.work[2 * item + 1];
@@ -253,7 +263,6 @@ void bwd_dkdv_kernel(BwdArgs a) {
   // K and V of block b staged in LDS as [key][dim] rows (16-byte chunk p of
   // row r at slot p ^ (r & 7), so 8 consecutive rows read together hit
   // distinct banks); keys past the sequence are zero rows.
-  __shared__ __attribute__((aligned(16))) uint8_t kv[2][64 * 256];
   {
     const int64_t gstride = (int64_t)a.h_kv * kHeadDim;
     const uint16_t* kb = a.k + (((int64_t)rk.start + kBlock * b) * a.h_kv + g) * kHeadDim;
@@ -274,9 +283,41 @@ void bwd_dkdv_kernel(BwdArgs a) {
         *reinterpret_cast<u32x4*>(kv[1] + part * 1024 + 16 * lane) = xv;
       }
     }
-    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
   }
+
+  // The item's tokens: ordinals [chunk * kBwdChunk, +kBwdChunk) of the
+  // block's tokens in ascending (tile, row) order (the K / V loads are in
+  // flight meanwhile).
+  const uint16_t* mrow = a.mask_b + (int64_t)e * a.ntiles;
+  const int ntile_s = min((rq.len + 15) / 16, a.ntiles);
+  const int target = chunk * kBwdChunk, target_end = target + kBwdChunk;
+  int run = 0;
+  for (int tau = max(0, kBlock * b - pos0) / 16; tau < ntile_s && run < target_end; tau += 64) {
+    const uint32_t m = tau + lane < ntile_s ? mrow[tau + lane] : 0u;
+    const int c = __builtin_popcount(m);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int tot = __shfl(incl, 63);
+    if (run + tot > target) {
+      int ord = run + incl - c;
+      uint32_t mm = m;
+      while (mm != 0u) {
+        const int bit = (int)__builtin_ctz(mm);
+        mm &= mm - 1;
+        if (ord >= target && ord < target_end) toks[ord - target] = 16 * (tau + lane) + bit;
+        ++ord;
+      }
+    }
+    run += tot;
+  }
+  const int count = max(0, min(run, target_end) - target);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  __syncthreads();
+
   // B operand (key tile kt, dims 32ks + 8q4 .. +7) of row 16kt + c16.
   auto frag = [&](int which, int kt, int ks) {
     const int row = 16 * kt + c16;
@@ -291,105 +332,122 @@ void bwd_dkdv_kernel(BwdArgs a) {
       dv[kt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-  auto token = [&](int i) {
+  const bool hv = c16 < a.G;
+  auto load = [&](int i, TokOps& o) {
     const int64_t r = (int64_t)rq.start + i;
-    const int t = pos0 + i;
-    const bool hv = c16 < a.G;
     const int64_t qoff = (r * a.h_q + (int64_t)g * a.G + c16) * kHeadDim + 8 * q4;
-    u32x4 qa[4], da[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      qa[ks] = hv ? ldg16(a.q + qoff + 32 * ks) : zero16();
-      da[ks] = hv ? ldg16(a.dout + qoff + 32 * ks) : zero16();
+      o.qa[ks] = hv ? ldg16(a.q + qoff + 32 * ks) : zero16();
+      o.da[ks] = hv ? ldg16(a.dout + qoff + 32 * ks) : zero16();
     }
     const int64_t soff = (r * a.h_kv + g) * 16 + 4 * q4;
-    const floatx4 l2 = *reinterpret_cast<const floatx4*>(a.lse2 + soff);
-    const floatx4 dd = *reinterpret_cast<const floatx4*>(a.dd + soff);
-    // S, dP and the bf16 P^T, dS^T of the four key tiles ...
+    o.l2 = *reinterpret_cast<const floatx4*>(a.lse2 + soff);
+    o.dd = *reinterpret_cast<const floatx4*>(a.dd + soff);
+  };
+  auto compute = [&](int i, const TokOps& o) {
+    const int t = pos0 + i;
+    u32x4 oqt[4], odt[4];
+    {
+      const int64_t toff = (((int64_t)rq.start + i) * a.h_kv + g) * 2048 + (c16 * 4 + q4) * 32;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        oqt[m] = ldg16(a.qt + toff + 8 * m);
+        odt[m] = ldg16(a.dot + toff + 8 * m);
+      }
+    }
     s16x4 pa[4], dsa[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       floatx4 sc = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        sc = mfma16(as_bf16x8(qa[ks]), frag(0, kt, ks), sc);
-        dp = mfma16(as_bf16x8(da[ks]), frag(1, kt, ks), dp);
+        sc = mfma16(as_bf16x8(o.qa[ks]), frag(0, kt, ks), sc);
+        dp = mfma16(as_bf16x8(o.da[ks]), frag(1, kt, ks), dp);
       }
       const bool vis = kBlock * b + 16 * kt + c16 <= t;
       float p[4], ds[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        p[j] = vis ? fast_exp2(fmaf(sc[j], a.c, -l2[j])) : 0.f;
-        ds[j] = vis ? p[j] * (dp[j] - dd[j]) : 0.f;
+        p[j] = vis ? fast_exp2(fmaf(sc[j], a.c, -o.l2[j])) : 0.f;
+        ds[j] = vis ? p[j] * (dp[j] - o.dd[j]) : 0.f;
       }
       pa[kt] = pack4(p[0], p[1], p[2], p[3]);
       dsa[kt] = pack4(ds[0], ds[1], ds[2], ds[3]);
     }
-    // ... then the head contractions, one 16-dim slice of Q^T / dO^T at a time.
-    const int64_t toff = ((r * a.h_kv + g) * kHeadDim + c16) * 16 + 4 * q4;
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      const s16x4 qt = *reinterpret_cast<const s16x4*>(a.qt + toff + 256 * dt);
-      const s16x4 dot = *reinterpret_cast<const s16x4*>(a.dot + toff + 256 * dt);
+    for (int m = 0; m < 4; ++m) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        dv[kt][dt] = mfma16k16(pa[kt], dot, dv[kt][dt]);
-        dk[kt][dt] = mfma16k16(dsa[kt], qt, dk[kt][dt]);
+      for (int h = 0; h < 2; ++h) {
+        const int dt = 2 * m + h;
+        const s16x4 qt = __builtin_bit_cast(s16x4, uint2{oqt[m][2 * h], oqt[m][2 * h + 1]});
+        const s16x4 dot = __builtin_bit_cast(s16x4, uint2{odt[m][2 * h], odt[m][2 * h + 1]});
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) {
+          dv[kt][dt] = mfma16k16(pa[kt], dot, dv[kt][dt]);
+          dk[kt][dt] = mfma16k16(dsa[kt], qt, dk[kt][dt]);
+        }
       }
     }
   };
 
-  // Token ordinals [chunk * kBwdChunk, +kBwdChunk) of the block's tokens in
-  // ascending (tile, row) order.
-  const uint16_t* mrow = a.mask_b + (int64_t)e * a.ntiles;
-  const int ntile_s = min((rq.len + 15) / 16, a.ntiles);
-  const int target = chunk * kBwdChunk, target_end = target + kBwdChunk;
-  int tau = max(0, kBlock * b - pos0) / 16;
-  int run = 0;
-  for (; tau < ntile_s; tau += 64) {
-    const uint32_t m = tau + lane < ntile_s ? mrow[tau + lane] : 0u;
-    int tot = __builtin_popcount(m);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) tot += __shfl_xor(tot, o);
-    if (run + tot > target) break;
-    run += tot;
-  }
-  int ord = run;
-  for (; tau < ntile_s && ord < target_end; tau += 64) {
-    const uint32_t m = tau + lane < ntile_s ? mrow[tau + lane] : 0u;
-    uint64_t nz = __ballot(m != 0u);
-    while (nz != 0 && ord < target_end) {
-      const int l = (int)__builtin_ctzll(nz);
-      nz &= nz - 1;
-      uint32_t mm = __builtin_amdgcn_readlane(m, l);
-      const int cnt = __builtin_popcount(mm);
-      if (ord + cnt <= target) {
-        ord += cnt;
-        continue;
-      }
-      while (mm != 0 && ord < target_end) {
-        const int bit = (int)__builtin_ctz(mm);
-        mm &= mm - 1;
-        if (ord >= target) token(16 * (tau + l) + bit);
-        ++ord;
-      }
+  TokOps A, B;
+  if (count > 0) load(toks[0], A);
+  for (int x = 0; x < count; x += 2) {
+    if (x + 1 < count) load(toks[x + 1], B);
+    compute(toks[x], A);
+    if (x + 1 < count) {
+      if (x + 2 < count) load(toks[x + 2], A);
+      compute(toks[x + 1], B);
     }
   }
 
+  // Partial sums of this item: floatx4 (which, kt, dt) of every lane, lane-major.
+  float* part = a.part + (int64_t)item * 16384 + 4 * lane;
 #pragma unroll
-  for (int kt = 0; kt < 4; ++kt) {
+  for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = kBlock * b + 16 * kt + 4 * q4 + j;
-      if (key >= rk.len || (int64_t)rk.start + key >= a.rows_k) continue;
-      float* pk = a.dk_acc + (((int64_t)rk.start + key) * a.h_kv + g) * kHeadDim + c16;
-      float* pv = a.dv_acc + (((int64_t)rk.start + key) * a.h_kv + g) * kHeadDim + c16;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-        unsafeAtomicAdd(pk + 16 * dt, a.scale * dk[kt][dt][j]);
-        unsafeAtomicAdd(pv + 16 * dt, dv[kt][dt][j]);
-      }
+    for (int dt = 0; dt < 8; ++dt) {
+      *reinterpret_cast<floatx4*>(part + (kt * 8 + dt) * 256) = dk[kt][dt] * a.scale;
+      *reinterpret_cast<floatx4*>(part + ((4 + kt) * 8 + dt) * 256) = dv[kt][dt];
     }
+}
+
+// ---------------------------------------------------------------------------
+// Pass 4: dK (blockIdx.y = 0) or dV (1) of one block: the partial sums of its
+// items added in item order, rounded to bf16, written row by row.  Blocks no
+// row attends get zeros.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
+  __shared__ float blk[64][kHeadDim + 4];
+  const int e = blockIdx.x, which = blockIdx.y;
+  const int b = e % a.nblk;
+  const int gs = e / a.nblk;
+  const int s = gs % a.batch, g = gs / a.batch;
+  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
+  if (kBlock * b >= rk.len) return;
+  const int n_items = a.items[e], first = a.item_off[e];
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int f = tid + 256 * k;             // (kt, dt) = f / 64, lane = f % 64
+    const int kt = f >> 9, dt = (f >> 6) & 7, ln = f & 63;
+    floatx4 acc = floatx4{0.f, 0.f, 0.f, 0.f};
+    const float* src = a.part + (int64_t)first * 16384 + ((which * 4 + kt) * 8 + dt) * 256 + 4 * ln;
+    for (int j = 0; j < n_items; ++j) acc += *reinterpret_cast<const floatx4*>(src + (int64_t)j * 16384);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) blk[16 * kt + 4 * (ln >> 4) + jj][16 * dt + (ln & 15)] = acc[jj];
+  }
+  __syncthreads();
+  uint16_t* dst = which ? a.dv : a.dk;
+  for (int c = tid; c < 64 * 16; c += 256) {
+    const int row = c >> 4, ch = c & 15;
+    const int key = kBlock * b + row;
+    if (key >= rk.len || (int64_t)rk.start + key >= a.rows_k) continue;
+    const float* x = &blk[row][8 * ch];
+    stg16(dst + (((int64_t)rk.start + key) * a.h_kv + g) * kHeadDim + 8 * ch,
+          u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                pack_bf16x2(x[6], x[7])});
   }
 }
 
@@ -724,36 +782,11 @@ __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a) {
   st.run(sh);
 }
 
-// Pass 4: fp32 key gradients -> bf16 for the rows of every sequence.
-// Grid (ceil(max_k / 64), batch); each thread rounds 8 values.
-__global__ __launch_bounds__(256) void bwd_convert_kernel(BwdArgs a) {
-  const int s = blockIdx.y;
-  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
-  const int per_row = a.h_kv * kHeadDim / 8;
-  for (int i = threadIdx.x; i < kBlock * per_row; i += 256) {
-    const int key = blockIdx.x * kBlock + i / per_row;
-    if (key >= rk.len || (int64_t)rk.start + key >= a.rows_k) continue;
-    const int64_t off = ((int64_t)rk.start + key) * a.h_kv * kHeadDim + 8 * (i % per_row);
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-      const float* src = (which ? a.dv_acc : a.dk_acc) + off;
-      const floatx4 x = *reinterpret_cast<const floatx4*>(src);
-      const floatx4 y = *reinterpret_cast<const floatx4*>(src + 4);
-      stg16((which ? a.dv : a.dk) + off,
-            u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(y[0], y[1]),
-                  pack_bf16x2(y[2], y[3])});
-    }
-  }
-}
-
 }  // namespace
 
 hipError_t launch_attention_bwd(const BwdArgs& a, int max_seqlen_q, int max_seqlen_k, hipStream_t st) {
+  (void)max_seqlen_k;
   hipLaunchKernelGGL(bwd_prep_kernel, dim3((unsigned)((a.rows_q + 3) / 4), a.h_kv), dim3(256), 0, st, a);
-  const int64_t nacc = a.rows_k * a.h_kv * kHeadDim;
-  const unsigned zg = (unsigned)std::min<int64_t>((nacc + 255) / 256, 65536);
-  hipLaunchKernelGGL(bwd_zero_kernel, dim3(zg), dim3(256), 0, st, a.dk_acc, nacc);
-  hipLaunchKernelGGL(bwd_zero_kernel, dim3(zg), dim3(256), 0, st, a.dv_acc, nacc);
   hipLaunchKernelGGL(bwd_mask_kernel, dim3(a.ntiles, a.h_kv, a.batch), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_mask_transpose_kernel, dim3((a.nblk + 63) / 64, (a.ntiles + 63) / 64, a.h_kv * a.batch),
                      dim3(256), 0, st, a);
@@ -761,7 +794,7 @@ hipError_t launch_attention_bwd(const BwdArgs& a, int max_seqlen_q, int max_seql
   hipLaunchKernelGGL(bwd_list_kernel, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.wmax), dim3(64), 0, st, a);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((max_seqlen_q + 15) / 16, a.h_kv, a.batch), dim3(kDqThreads), 0, st, a);
-  hipLaunchKernelGGL(bwd_convert_kernel, dim3((max_seqlen_k + kBlock - 1) / kBlock, a.batch), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((int64_t)a.h_kv * a.batch * a.nblk), 2), dim3(256), 0, st, a);
   return hipGetLastError();
 }
 

@@ -135,14 +135,15 @@ struct BwdArgs {
   // workspace
   float* lse2;              // [rows_q, h_kv, 16] LSE * log2(e) per padded head (+inf: no keys / pad)
   float* dd;                // [rows_q, h_kv, 16] D = dO . O per padded head
-  uint16_t* qt;             // [rows_q, h_kv, 128, 16] Q as [dim][head] per (row, group)
-  uint16_t* dot;            // [rows_q, h_kv, 128, 16] dO likewise
-  float* dk_acc;            // [rows_k, h_kv, 128]
-  float* dv_acc;
+  uint16_t* qt;             // [rows_q, h_kv, 2048] Q per (row, group) in the lane order of
+                            // the head-contracting MFMA operand: [c16][q4][dt][4 heads]
+  uint16_t* dot;            // dO likewise
+  float* part;              // [wmax, 16384] fp32 dK / dV partial sums of each work item
   uint16_t* mask_t;         // [h_kv, batch, ntiles, nblk] tokens of a 16-row tile per block
   uint16_t* mask_b;         // [h_kv, batch, nblk, ntiles] the same, block-major
   int ntiles, nblk;         // per-sequence maxima: ceil(max_q / 16), ceil(max_k / 64)
   int32_t* items;           // [h_kv, batch, nblk] work items per block
+  int32_t* item_off;        // [h_kv, batch, nblk] index of each block's first item
   int32_t* work;            // [wmax, 2] (block index, item within the block)
   int32_t* nwork;           // number of work items
   int wmax;
