@@ -18,10 +18,9 @@
 //     read as a set; dense: every causal block), transposed block-major;
 //     token counts per block split into work items of at most kBwdChunk
 //     tokens;
-//  3. dK / dV, key-major: one wave per work item stages its K / V block in
-//     LDS, streams the item's tokens (ascending, the next token's operands in
-//     flight while the current one computes) and stores its fp32 partial
-//     sums; dQ, query-major: the forward's tile layout, each block a tile's
+//  3. dK / dV, key-major: per work item two waves (half of the dims each)
+//     stage its K / V block in LDS, stream the item's tokens (ascending) and
+//     store their fp32 partial sums; dQ, query-major: the forward's tile layout, each block a tile's
 //     tokens attend staged once in LDS;
 //  4. each block's partial sums are added in item order (deterministic) and
 //     rounded to bf16.
@@ -227,49 +226,49 @@ __global__ __launch_bounds__(1024) void bwd_list_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Pass 3a: dK, dV of one block for the tokens of one work item, one wave
-// (its 64 x 128 fp32 dK and dV sums fill the register file: one wave per SIMD).
-// Products with heads on the 16-wide side:
+// Pass 3a: dK, dV of one block for the tokens of one work item.  Two waves:
+// wave w owns dims 64w .. 64w+63 of the block's 64 x 128 dK and dV (128 fp32
+// registers), so two such workgroups fit on a SIMD pair per slot.  Products
+// with heads on the 16-wide side:
 //   S  = Q K^T        (16 heads x 16 keys per MFMA, contraction over dims)
 //   dP = dO V^T
 //   dV += P^T dO,  dK += dS^T Q   (16 keys x 16 dims, contraction over heads)
 // S and dP come out with lane (c16 = key, q4 -> heads 4*q4 .. +3), exactly
 // the A layout of the head-contracting 16x16x16 products, whose B operands
-// are the lane-ordered copies of Q and dO written by pass 1.  The item's
-// tokens are listed in LDS first; the loop then keeps the next token's
-// operands in flight while the current one computes.  The partial sums go
-// to the item's own slot of the workspace (no atomics).
+// are the lane-ordered copies of Q and dO written by pass 1.  Both waves
+// compute S and dP (the full contraction over dims) from the K / V block
+// staged once in LDS; the item's tokens are listed in LDS first.  The
+// partial sums go to the item's own slot of the workspace (no atomics).
 // ---------------------------------------------------------------------------
-struct TokOps {
-  u32x4 qa[4], da[4];       // Q, dO rows as A operands (dims 32ks + 8q4 .. +7 of head c16)
-  floatx4 l2, dd;           // LSE * log2(e) and D of heads 4q4 .. +3
-};
+constexpr int kDkvWaves = 2;
 
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void bwd_dkdv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * kDkvWaves) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t kv[2][64 * 256];
   __shared__ int32_t toks[kBwdChunk];
+  __shared__ int32_t tok_count;
   const int item = blockIdx.x;
   if (item >= *a.nwork) return;
   const int e = a.work[2 * item], chunk = a.work[2 * item + 1];
   const int b = e % a.nblk;
   const int gs = e / a.nblk;
   const int s = gs % a.batch, g = gs / a.batch;
-  const int lane = threadIdx.x, q4 = lane >> 4, c16 = lane & 15;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q4 = lane >> 4, c16 = lane & 15;
   const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
   const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
   const int pos0 = rk.len - rq.len;
 
   // K and V of block b staged in LDS as [key][dim] rows (16-byte chunk p of
   // row r at slot p ^ (r & 7), so 8 consecutive rows read together hit
-  // distinct banks); keys past the sequence are zero rows.
+  // distinct banks); keys past the sequence are zero rows.  Each wave stages
+  // 8 of the 16 parts of 4 rows.
   {
     const int64_t gstride = (int64_t)a.h_kv * kHeadDim;
     const uint16_t* kb = a.k + (((int64_t)rk.start + kBlock * b) * a.h_kv + g) * kHeadDim;
     const uint16_t* vb = a.v + (((int64_t)rk.start + kBlock * b) * a.h_kv + g) * kHeadDim;
     const bool inside = kBlock * b + kBlock <= rk.len && (int64_t)rk.start + kBlock * b + kBlock <= a.rows_k;
 #pragma unroll
-    for (int part = 0; part < 16; ++part) {
+    for (int j = 0; j < 16 / kDkvWaves; ++j) {
+      const int part = wave + kDkvWaves * j;
       const int row = 4 * part + (lane >> 4);
       const int64_t off = row * gstride + 8 * ((lane & 15) ^ (row & 7));
       if (inside) {
@@ -285,55 +284,64 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // The item's tokens: ordinals [chunk * kBwdChunk, +kBwdChunk) of the
-  // block's tokens in ascending (tile, row) order (the K / V loads are in
-  // flight meanwhile).
-  const uint16_t* mrow = a.mask_b + (int64_t)e * a.ntiles;
-  const int ntile_s = min((rq.len + 15) / 16, a.ntiles);
-  const int target = chunk * kBwdChunk, target_end = target + kBwdChunk;
-  int run = 0;
-  for (int tau = max(0, kBlock * b - pos0) / 16; tau < ntile_s && run < target_end; tau += 64) {
-    const uint32_t m = tau + lane < ntile_s ? mrow[tau + lane] : 0u;
-    const int c = __builtin_popcount(m);
-    int incl = c;
+  // The item's tokens (wave 0): ordinals [chunk * kBwdChunk, +kBwdChunk) of
+  // the block's tokens in ascending (tile, row) order.
+  if (wave == 0) {
+    const uint16_t* mrow = a.mask_b + (int64_t)e * a.ntiles;
+    const int ntile_s = min((rq.len + 15) / 16, a.ntiles);
+    const int target = chunk * kBwdChunk, target_end = target + kBwdChunk;
+    int run = 0;
+    for (int tau = max(0, kBlock * b - pos0) / 16; tau < ntile_s && run < target_end; tau += 64) {
+      const uint32_t m = tau + lane < ntile_s ? mrow[tau + lane] : 0u;
+      const int c = __builtin_popcount(m);
+      int incl = c;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
-    const int tot = __shfl(incl, 63);
-    if (run + tot > target) {
-      int ord = run + incl - c;
-      uint32_t mm = m;
-      while (mm != 0u) {
-        const int bit = (int)__builtin_ctz(mm);
-        mm &= mm - 1;
-        if (ord >= target && ord < target_end) toks[ord - target] = 16 * (tau + lane) + bit;
-        ++ord;
+      for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o);
+        if (lane >= o) incl += y;
       }
+      const int tot = __shfl(incl, 63);
+      if (run + tot > target) {
+        int ord = run + incl - c;
+        uint32_t mm = m;
+        while (mm != 0u) {
+          const int bit = (int)__builtin_ctz(mm);
+          mm &= mm - 1;
+          if (ord >= target && ord < target_end) toks[ord - target] = 16 * (tau + lane) + bit;
+          ++ord;
+        }
+      }
+      run += tot;
     }
-    run += tot;
+    if (lane == 0) tok_count = max(0, min(run, target_end) - target);
   }
-  const int count = max(0, min(run, target_end) - target);
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   __syncthreads();
+  const int count = tok_count;
 
   // B operand (key tile kt, dims 32ks + 8q4 .. +7) of row 16kt + c16.
   auto frag = [&](int which, int kt, int ks) {
     const int row = 16 * kt + c16;
     return as_bf16x8(*reinterpret_cast<const u32x4*>(kv[which] + row * 256 + (((4 * ks + q4) ^ (row & 7)) << 4)));
   };
-  floatx4 dk[4][8], dv[4][8];
+  floatx4 dk[4][4], dv[4][4];
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      dk[kt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-      dv[kt][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int dl = 0; dl < 4; ++dl) {
+      dk[kt][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
+      dv[kt][dl] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
   const bool hv = c16 < a.G;
-  auto load = [&](int i, TokOps& o) {
+  // Operands of one token; the next token's are in flight while the current
+  // one computes.
+  struct Ops {
+    u32x4 qa[4], da[4];     // Q, dO as A operands (dims 32ks + 8q4 .. +7 of head c16)
+    u32x4 qt[2], dt[2];     // this wave's dim tiles of Q, dO as [dim][head] B operands
+    floatx4 l2, dd;         // LSE * log2(e) and D of heads 4q4 .. +3
+  };
+  auto load = [&](int i, Ops& o) {
     const int64_t r = (int64_t)rq.start + i;
     const int64_t qoff = (r * a.h_q + (int64_t)g * a.G + c16) * kHeadDim + 8 * q4;
 #pragma unroll
@@ -341,21 +349,18 @@ void bwd_dkdv_kernel(BwdArgs a) {
       o.qa[ks] = hv ? ldg16(a.q + qoff + 32 * ks) : zero16();
       o.da[ks] = hv ? ldg16(a.dout + qoff + 32 * ks) : zero16();
     }
+    const int64_t toff = (r * a.h_kv + g) * 2048 + (c16 * 4 + q4) * 32 + 16 * wave;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      o.qt[m] = ldg16(a.qt + toff + 8 * m);
+      o.dt[m] = ldg16(a.dot + toff + 8 * m);
+    }
     const int64_t soff = (r * a.h_kv + g) * 16 + 4 * q4;
     o.l2 = *reinterpret_cast<const floatx4*>(a.lse2 + soff);
     o.dd = *reinterpret_cast<const floatx4*>(a.dd + soff);
   };
-  auto compute = [&](int i, const TokOps& o) {
+  auto compute = [&](int i, const Ops& o) {
     const int t = pos0 + i;
-    u32x4 oqt[4], odt[4];
-    {
-      const int64_t toff = (((int64_t)rq.start + i) * a.h_kv + g) * 2048 + (c16 * 4 + q4) * 32;
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        oqt[m] = ldg16(a.qt + toff + 8 * m);
-        odt[m] = ldg16(a.dot + toff + 8 * m);
-      }
-    }
     s16x4 pa[4], dsa[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
@@ -376,22 +381,21 @@ void bwd_dkdv_kernel(BwdArgs a) {
       dsa[kt] = pack4(ds[0], ds[1], ds[2], ds[3]);
     }
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
+    for (int m = 0; m < 2; ++m) {
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        const int dt = 2 * m + h;
-        const s16x4 qt = __builtin_bit_cast(s16x4, uint2{oqt[m][2 * h], oqt[m][2 * h + 1]});
-        const s16x4 dot = __builtin_bit_cast(s16x4, uint2{odt[m][2 * h], odt[m][2 * h + 1]});
+        const int dl = 2 * m + h;
+        const s16x4 qv = __builtin_bit_cast(s16x4, uint2{o.qt[m][2 * h], o.qt[m][2 * h + 1]});
+        const s16x4 dv4 = __builtin_bit_cast(s16x4, uint2{o.dt[m][2 * h], o.dt[m][2 * h + 1]});
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt) {
-          dv[kt][dt] = mfma16k16(pa[kt], dot, dv[kt][dt]);
-          dk[kt][dt] = mfma16k16(dsa[kt], qt, dk[kt][dt]);
+          dv[kt][dl] = mfma16k16(pa[kt], dv4, dv[kt][dl]);
+          dk[kt][dl] = mfma16k16(dsa[kt], qv, dk[kt][dl]);
         }
       }
     }
   };
-
-  TokOps A, B;
+  Ops A, B;
   if (count > 0) load(toks[0], A);
   for (int x = 0; x < count; x += 2) {
     if (x + 1 < count) load(toks[x + 1], B);
@@ -402,14 +406,16 @@ void bwd_dkdv_kernel(BwdArgs a) {
     }
   }
 
-  // Partial sums of this item: floatx4 (which, kt, dt) of every lane, lane-major.
+  // Partial sums of this item: floatx4 (which, kt, dt) of every lane,
+  // lane-major; this wave holds dim tiles dt = 4*wave + dl.
   float* part = a.part + (int64_t)item * 16384 + 4 * lane;
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt) {
-      *reinterpret_cast<floatx4*>(part + (kt * 8 + dt) * 256) = dk[kt][dt] * a.scale;
-      *reinterpret_cast<floatx4*>(part + ((4 + kt) * 8 + dt) * 256) = dv[kt][dt];
+    for (int dl = 0; dl < 4; ++dl) {
+      const int dtile = 4 * wave + dl;
+      *reinterpret_cast<floatx4*>(part + (kt * 8 + dtile) * 256) = dk[kt][dl] * a.scale;
+      *reinterpret_cast<floatx4*>(part + ((4 + kt) * 8 + dtile) * 256) = dv[kt][dl];
     }
 }
 
@@ -792,7 +798,7 @@ hipError_t launch_attention_bwd(const BwdArgs& a, int max_seqlen_q, int max_seql
                      dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_count_kernel, dim3((a.nblk + 3) / 4, a.h_kv, a.batch), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_list_kernel, dim3(1), dim3(1024), 0, st, a);
-  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.wmax), dim3(64), 0, st, a);
+  hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.wmax), dim3(64 * kDkvWaves), 0, st, a);
   hipLaunchKernelGGL(bwd_dq_kernel, dim3((max_seqlen_q + 15) / 16, a.h_kv, a.batch), dim3(kDqThreads), 0, st, a);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((int64_t)a.h_kv * a.batch * a.nblk), 2), dim3(256), 0, st, a);
   return hipGetLastError();
