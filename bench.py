@@ -137,6 +137,9 @@ def main():
                          "selection sizes |I| against the dense kernel at the same length; "
                          "backward: the gradients of the 128K sparse attention (selection "
                          "held fixed)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="decode: launch the step's kernels one by one instead of replaying "
+                         "the captured HIP graph of the step")
     ap.add_argument("--sel", type=str, default="16,32,64,96",
                     help="sweep: selection sizes |I| (1 init block, |I|//3 local, rest top-k)")
     args = ap.parse_args()
@@ -273,8 +276,10 @@ def main():
 def bench_decode(args):
     """Decode: batch 16, a 128K-token cache per sequence, one new token per
     sequence per step (incremental compress_k, select_blocks, sparse_attn:
-    the split-K path).  Timed per step with HIP events around the library
-    calls; the caller's cache append is outside the timed region."""
+    the split-K path), replayed as the captured HIP graph of the step
+    (--no-graph: the library calls one by one).  Timed per step with HIP
+    events around the replay (or the calls); the caller's cache append is
+    outside the timed region."""
     import torch
 
     from trainable_block_sparse_compress_amd import binding as B
@@ -296,11 +301,24 @@ def bench_decode(args):
     out = torch.empty((batch, h_q, d), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
     t_step, t_sel, t_attn = [], [], []
-    print("[bench] decode steps", file=sys.stderr, flush=True)
+    graph = None if args.no_graph else P.DecodeGraph(dec)
+    print(f"[bench] decode steps ({'eager' if graph is None else 'graph replay'})", file=sys.stderr,
+          flush=True)
     for i in range(nsteps):
         old = dec.append(ks[i], vs[i])
         dec.step_prepare(old)
         q_new = qs[i].contiguous()
+        if graph is not None:
+            graph.q.copy_(q_new)          # the caller's input placement, outside the timed region
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            graph.graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= args.warmup:
+                t_step.append(e0.elapsed_time(e1))
+            continue
         torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
         c, mx = cfg, max(dec.lens)
@@ -344,7 +362,9 @@ def bench_decode(args):
         "config": {"workload": f"decode, batch {batch}, cache {len0} per sequence, one token per "
                                "sequence per step", "h_q": h_q, "h_kv": h_kv, "head_dim": d,
                    "n_init": 1, "n_local": 32, "n_topk": 63, "lse": args.lse},
-        "ms_select_blocks": float(np.mean(t_sel)), "ms_sparse_attn": float(np.mean(t_attn)),
+        "launch": "eager" if graph is None else "HIP graph replay of the captured step",
+        "ms_select_blocks": float(np.mean(t_sel)) if t_sel else None,
+        "ms_sparse_attn": float(np.mean(t_attn)) if t_attn else None,
         "roofline": {"bound": "hbm", "kernel": "whole decode step (compress_k + select_blocks + "
                                                 "sparse_attn)",
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,

@@ -526,6 +526,39 @@ def test_decode_steps(lib, mode):
             assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (step, s, ma, rr)
 
 
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_decode_graph_replays_match_eager(lib, mode):
+    """The decode step captured once as a HIP graph and replayed for several
+    steps, with the caller's eager cache appends between replays, gives
+    bit-identical block lists and outputs to the eager step."""
+    say(f"decode graph {mode}")
+    batch, h_q, h_kv, steps = 3, 32, 2, 5
+    lens0 = [7000, 9001, 6400]
+    cap = 9088
+    cfg = _cfg(R.Params(lse_mode=mode))
+    inp = D.make_prefill(4, [cap] * batch, h_q, h_kv, n_needles=4)
+    st = _starts([cap] * batch)
+    kt, vt, qt = to_dev(inp.k), to_dev(inp.v), to_dev(inp.q)
+    decs = [P.DecodeState(batch, cap, h_q, h_kv, cfg) for _ in range(2)]
+    for dec in decs:
+        dec.fill([kt[st[s]:st[s] + lens0[s]] for s in range(batch)],
+                 [vt[st[s]:st[s] + lens0[s]] for s in range(batch)], lens0)
+    graph = P.DecodeGraph(decs[1])
+    out = torch.empty((batch, h_q, 128), dtype=torch.bfloat16, device="cuda")
+    for step in range(steps):
+        pos = [decs[0].lens[s] for s in range(batch)]
+        k_new = torch.stack([kt[st[s] + pos[s]] for s in range(batch)])
+        v_new = torch.stack([vt[st[s] + pos[s]] for s in range(batch)])
+        q_new = torch.stack([qt[st[s] + pos[s]] for s in range(batch)]).contiguous()
+        for dec in decs:
+            dec.step_prepare(dec.append(k_new, v_new))
+        decs[0].step(q_new, out, max(decs[0].lens))
+        got = graph.step(q_new)
+        torch.cuda.synchronize()
+        assert torch.equal(decs[0].block_idx, decs[1].block_idx), step
+        assert torch.equal(out.view(torch.int16), got.view(torch.int16)), step
+
+
 def test_deterministic(lib):
     say("determinism")
     n = 8192

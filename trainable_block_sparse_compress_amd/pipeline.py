@@ -18,7 +18,7 @@ import torch
 from . import binding as B
 
 __all__ = ["SparseConfig", "n_windows", "SparsePlan", "DensePlan", "SwitchPlan", "attention",
-           "DecodeState"]
+           "DecodeState", "DecodeGraph"]
 
 
 @dataclass(frozen=True)
@@ -270,3 +270,31 @@ class DecodeState:
         B.sparse_attn(q_new, self.k_cache, self.vt_cache, self.cu_q, self.used_q, self.cu_k,
                       self.used_k, self.batch, 1, max_len, self.block_idx, c.n_init, c.n_local,
                       c.scale(self.d), out, None, self.ws_attn, v_seq_stride=self.cap)
+
+
+class DecodeGraph:
+    """One decode step of a ``DecodeState`` captured as a HIP graph.
+
+    The step is kernel launches only (the library allocates, frees and
+    synchronises nothing), so it captures as is.  It is captured with the
+    cache capacity as the maximum key length: grids cover the capacity and
+    every kernel takes the actual lengths from the device metadata that
+    ``append`` / ``step_prepare`` update, so one capture serves every step.
+    ``step`` copies the new queries into the captured input buffer and
+    replays; the result is in ``out``.
+    """
+
+    def __init__(self, dec: DecodeState):
+        self.dec = dec
+        dev = dec.k_cache.device
+        self.q = torch.zeros((dec.batch, dec.h_q, dec.d), dtype=torch.bfloat16, device=dev)
+        self.out = torch.zeros_like(self.q)
+        self.graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self.graph):
+            dec.step(self.q, self.out, dec.cap)
+
+    def step(self, q_new):
+        self.q.copy_(q_new)
+        self.graph.replay()
+        return self.out
