@@ -129,14 +129,15 @@ def main():
                          "kernel of known size, to calibrate HBM byte counters)")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="also time the dense causal kernel at the same length (context)")
-    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep", "backward"],
+    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep", "backward", "layer"],
                     default="prefill",
                     help="prefill (default): one 128K sequence; decode: 16 sequences x 128K "
                          "cache, one token each per step; varlen: 65536 packed tokens of mixed "
                          "lengths through the dense/sparse switch; sweep: the prefill at several "
                          "selection sizes |I| against the dense kernel at the same length; "
                          "backward: the gradients of the 128K sparse attention (selection "
-                         "held fixed)")
+                         "held fixed); layer: one attention layer of the 8B shape (hidden 4096) "
+                         "with its Q/K/V/O projections, sparse against dense")
     ap.add_argument("--no-graph", action="store_true",
                     help="decode: launch the step's kernels one by one instead of replaying "
                          "the captured HIP graph of the step")
@@ -156,6 +157,8 @@ def main():
         return bench_sweep(args)
     if args.workload == "backward":
         return bench_backward(args)
+    if args.workload == "layer":
+        return bench_layer(args)
 
     import torch
 
@@ -624,6 +627,90 @@ def bench_backward(args):
         "roofline": {"bound": "mfma", "kernel": "whole backward (infllmv2_sparse_attn_bwd)",
                      "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": tf / PEAK_BF16_TFLOPS, "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_layer(args):
+    """One attention layer of the 8B GQA shape the pages evaluate (hidden
+    4096, 32 query heads, 2 KV heads, head_dim 128) at prefill length n:
+    Q/K/V projections of a seeded hidden state (random weights; library
+    GEMMs), then either the sparse path (compress_k, select_blocks,
+    sparse_attn) or the dense kernel, then the output projection.  Time to
+    first token of one layer, sparse against dense (the pages' end-to-end
+    prefill comparison measures whole models; FFN and norms are not part of
+    the attention path and are left out)."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    n, hidden, h_q, h_kv, d = args.seq, 4096, 32, 2, 128
+    print(f"[bench] layer inputs n={n}", file=sys.stderr, flush=True)
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    bf = torch.bfloat16
+    x = torch.randn((n, hidden), generator=gen, device="cuda", dtype=torch.float32).to(bf)
+    w = lambda o: (torch.randn((hidden, o), generator=gen, device="cuda", dtype=torch.float32)
+                   / math.sqrt(hidden)).to(bf)
+    wq, wk, wv = w(h_q * d), w(h_kv * d), w(h_kv * d)    # stored [in, out]: no transposed operand
+    wo = (torch.randn((h_q * d, hidden), generator=gen, device="cuda", dtype=torch.float32)
+          / math.sqrt(h_q * d)).to(bf)
+    cfg = P.SparseConfig(lse_mode=args.lse)
+    plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
+    dplan = P.DensePlan([0], [n], [0], [n], n, h_q, h_kv, cfg, "cuda", d)
+    ws = torch.empty(max(1, B.attn_workspace(h_q, h_kv, 1, n, n, n, n_sel=cfg.n_sel,
+                                             n_init=cfg.n_init, n_local=cfg.n_local)),
+                     dtype=torch.uint8, device="cuda")
+    wsd = torch.empty(max(1, B.attn_workspace(h_q, h_kv, 1, n, n, n)), dtype=torch.uint8,
+                      device="cuda")
+    out = torch.empty((n, h_q, d), dtype=bf, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def layer(sparse):
+        q = (x @ wq).view(n, h_q, d)
+        k = (x @ wk).view(n, h_kv, d)
+        v = (x @ wv).view(n, h_kv, d)
+        if sparse:
+            plan.compress(k)
+            plan.select(q)
+            B.sparse_attn(q, k, v, plan.cu_q, plan.used_q, plan.cu_k, plan.used_k, 1, n, n,
+                          plan.block_idx, cfg.n_init, cfg.n_local, cfg.scale(d), out, None, ws)
+        else:
+            B.dense_attn(q, k, v, dplan.cu_q, dplan.used_q, dplan.cu_k, dplan.used_k, 1, n, n,
+                         cfg.scale(d), out, None, wsd)
+        return out.view(n, h_q * d) @ wo
+
+    def timed(sparse, reps):
+        layer(sparse)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            layer(sparse)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    print("[bench] sparse layer", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        layer(True)
+    ms_sparse = timed(True, args.steps)
+    print("[bench] dense layer", file=sys.stderr, flush=True)
+    ms_dense = timed(False, max(1, args.dense_steps or 2))
+    proj_flops = 2.0 * n * hidden * (h_q * d + 2 * h_kv * d) + 2.0 * n * h_q * d * hidden
+    res = {
+        "metric": f"attention-layer prefill tokens/s at n={n} (hidden 4096, 32q/2kv, d128, "
+                  "|I|=96, with Q/K/V/O projections)",
+        "value": n / (ms_sparse * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_sparse, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) hidden state, random projection weights",
+        "config": {"workload": f"one attention layer (projections + sparse path), n={n}",
+                   "seq_len": n, "hidden": hidden, "h_q": h_q, "h_kv": h_kv, "head_dim": d,
+                   "lse": args.lse},
+        "ms_dense_layer": ms_dense, "layer_speedup_vs_dense": ms_dense / ms_sparse,
+        "projection_flops": proj_flops,
+        "roofline": None,
     }
     print(json.dumps(res), flush=True)
 
