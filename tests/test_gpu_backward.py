@@ -216,3 +216,38 @@ def test_backward_full_size_sampled(lib, n):
         say(f"  group {g}: |sum dv - sum dO| / sum|dv| {dv_err.max():.2e}, "
             f"|sum dk| / sum|dk| {dk_err.max():.2e}")
         assert dv_err.max() <= 1e-2 and dk_err.max() <= 1e-2, (g, dv_err.max(), dk_err.max())
+
+
+def test_autograd_switch_matches_direct_calls(lib):
+    """attention_trainable: torch autograd through the switch (one dense and
+    one sparse sequence) gives exactly the gradients of the direct backward
+    calls, and the dense sequence's gradients match the oracle."""
+    say("autograd switch")
+    lengths, h_q, h_kv = [700, 2500], 4, 2
+    cfg = P.SparseConfig(n_init=1, n_local=4, n_topk=6, threshold=1024)
+    inp = D.make_prefill(48, lengths, h_q, h_kv)
+    dO = D.make_grad(49, sum(lengths), h_q)
+    q, k, v = (to_dev(x).requires_grad_(True) for x in (inp.q, inp.k, inp.v))
+    w = to_dev(dO)
+    plan = P.SwitchPlan(lengths, h_q, h_kv, cfg)
+    out = P.attention_trainable(q, k, v, lengths, cfg, plan=plan)
+    (out.float() * w.float()).sum().backward()
+    torch.cuda.synchronize()
+    # direct calls on the same plan and inputs
+    o2 = torch.empty_like(out)
+    lse = torch.empty((h_q, sum(lengths)), dtype=torch.float32, device="cuda")
+    qd, kd, vd = q.detach(), k.detach(), v.detach()
+    plan.run(qd, kd, vd, o2, lse)
+    dq, dk, dv = torch.zeros_like(qd), torch.zeros_like(kd), torch.zeros_like(vd)
+    plan.backward(qd, kd, vd, o2, lse, w, dq, dk, dv)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach().view(torch.int16), o2.view(torch.int16))
+    for got, want in ((q.grad, dq), (k.grad, dk), (v.grad, dv)):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    n0 = lengths[0]
+    rq, rk, rv = R.attention_grad(inp.q[:n0], inp.k[:n0], inp.v[:n0], dO[:n0], h_q // h_kv,
+                                  R.Params(), dense=True)
+    for name, got, ref in (("dq", q.grad[:n0], rq), ("dk", k.grad[:n0], rk), ("dv", v.grad[:n0], rv)):
+        mr, rr = grad_errors(to_f64(got), ref)
+        say(f"  dense sequence {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+        assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (name, mr, rr)

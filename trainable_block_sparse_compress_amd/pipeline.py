@@ -18,7 +18,7 @@ import torch
 from . import binding as B
 
 __all__ = ["SparseConfig", "n_windows", "SparsePlan", "DensePlan", "SwitchPlan", "attention",
-           "DecodeState", "DecodeGraph"]
+           "DecodeState", "DecodeGraph", "attention_trainable"]
 
 
 @dataclass(frozen=True)
@@ -120,6 +120,22 @@ class SparsePlan:
         self.select(q)
         self.attend(q, k, v, out, lse)
 
+    def backward(self, q, k, v, out, lse, dout, dq, dk, dv):
+        """Gradients of the last ``run`` (its block lists held fixed) into
+        dq, dk, dv (rows of these sequences); the workspace is allocated on
+        first use and kept."""
+        if self.batch == 0:
+            return
+        c = self.cfg
+        if getattr(self, "ws_bwd", None) is None:
+            size = B.attn_bwd_workspace(q.shape[1], k.shape[1], self.batch, self.max_q, self.max_k,
+                                        q.shape[0], k.shape[0], n_sel=c.n_sel, n_init=c.n_init,
+                                        n_local=c.n_local)
+            self.ws_bwd = torch.empty(max(1, size), dtype=torch.uint8, device=q.device)
+        B.sparse_attn_bwd(q, k, v, out, lse, dout, self.cu_q, self.used_q, self.cu_k, self.used_k,
+                          self.batch, self.max_q, self.max_k, self.block_idx, c.n_init, c.n_local,
+                          c.scale(self.d), dq, dk, dv, self.ws_bwd, block_size=c.block_size)
+
 
 class DensePlan:
     """Dense causal attention for the given sequences."""
@@ -142,6 +158,18 @@ class DensePlan:
             return
         B.dense_attn(q, k, v, self.cu_q, self.used_q, self.cu_k, self.used_k, self.batch,
                      self.max_q, self.max_k, self.cfg.scale(self.d), out, lse, self.ws)
+
+    def backward(self, q, k, v, out, lse, dout, dq, dk, dv):
+        """Gradients of the dense causal attention of these sequences."""
+        if self.batch == 0:
+            return
+        if getattr(self, "ws_bwd", None) is None:
+            size = B.attn_bwd_workspace(q.shape[1], k.shape[1], self.batch, self.max_q, self.max_k,
+                                        q.shape[0], k.shape[0])
+            self.ws_bwd = torch.empty(max(1, size), dtype=torch.uint8, device=q.device)
+        B.sparse_attn_bwd(q, k, v, out, lse, dout, self.cu_q, self.used_q, self.cu_k, self.used_k,
+                          self.batch, self.max_q, self.max_k, None, 0, 0, self.cfg.scale(self.d),
+                          dq, dk, dv, self.ws_bwd)
 
 
 class SwitchPlan:
@@ -168,6 +196,12 @@ class SwitchPlan:
         self.dense.run(q, k, v, out, lse)
         self.sparse.run(q, k, v, out, lse)
 
+    def backward(self, q, k, v, out, lse, dout, dq, dk, dv):
+        """Gradients of the last ``run``; dense and sparse sequences write
+        disjoint rows of dq, dk, dv."""
+        self.dense.backward(q, k, v, out, lse, dout, dq, dk, dv)
+        self.sparse.backward(q, k, v, out, lse, dout, dq, dk, dv)
+
 
 def attention(q, k, v, seqlens, cfg: SparseConfig | None = None, lse=None):
     """InfLLM-V2 attention of a packed prefill batch; returns the output."""
@@ -176,6 +210,37 @@ def attention(q, k, v, seqlens, cfg: SparseConfig | None = None, lse=None):
     out = torch.empty_like(q)
     plan.run(q, k, v, out, lse)
     return out
+
+
+class _SwitchAttention(torch.autograd.Function):
+    """Forward through the switch's kernels (the sparse sequences' block lists
+    from select_blocks), backward through infllmv2_sparse_attn_bwd on the same
+    lists: the selection is held fixed, so no gradient reaches the scoring."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, plan):
+        out = torch.empty_like(q)
+        lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
+        plan.run(q, k, v, out, lse)
+        ctx.save_for_backward(q, k, v, out, lse)
+        ctx.plan = plan
+        return out
+
+    @staticmethod
+    def backward(ctx, dout):
+        q, k, v, out, lse = ctx.saved_tensors
+        dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
+        ctx.plan.backward(q, k, v, out, lse, dout.to(torch.bfloat16).contiguous(), dq, dk, dv)
+        return dq, dk, dv, None
+
+
+def attention_trainable(q, k, v, seqlens, cfg: SparseConfig | None = None, plan=None):
+    """``attention`` with gradients (packed prefill batch, q/k/v bf16 with
+    requires_grad).  Pass a SwitchPlan built for these lengths to reuse its
+    buffers and workspaces across steps."""
+    cfg = cfg or SparseConfig()
+    plan = plan or SwitchPlan(seqlens, q.shape[1], k.shape[1], cfg, q.device, q.shape[2])
+    return _SwitchAttention.apply(q, k, v, plan)
 
 
 class DecodeState:
