@@ -251,3 +251,63 @@ def test_autograd_switch_matches_direct_calls(lib):
         mr, rr = grad_errors(to_f64(got), ref)
         say(f"  dense sequence {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
         assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (name, mr, rr)
+
+
+def test_backward_chunked_queries_and_empty_sequence(lib):
+    """Queries that are the last rows of longer key sequences (bottom-right
+    causal, as in chunked prefill), an empty sequence in the batch, and
+    scrambled lists: gradients against the oracle."""
+    say("backward chunked queries")
+    klens, qlens, h_q, h_kv = [1500, 0, 900], [300, 0, 900], 16, 2
+    p = R.Params(n_init=1, n_local=3, n_topk=5)
+    inp = D.make_prefill(50, klens, h_q, h_kv)
+    kst = _starts(klens)
+    qrows = [kst[s] + klens[s] - qlens[s] + i for s in range(3) for i in range(qlens[s])]
+    qst = _starts(qlens)
+    Q = np.ascontiguousarray(inp.q[qrows])
+    dO = D.make_grad(51, len(qrows), h_q)
+    rng = np.random.Generator(np.random.PCG64(52))
+    idx = np.full((h_kv, len(qrows), p.n_topk + 2), -1, dtype=np.int32)
+    sets = {}
+    for s in range(3):
+        for i in range(qlens[s]):
+            t = klens[s] - qlens[s] + i
+            bt = t // 64
+            fixed = set(range(min(p.n_init, bt + 1))) | set(range(max(0, bt - p.n_local + 1), bt + 1))
+            for g in range(h_kv):
+                rest = [b for b in range(bt + 1) if b not in fixed]
+                pick = rng.choice(rest, size=min(len(rest), p.n_topk), replace=False).tolist() if rest else []
+                row = pick + [-1, bt + 2]
+                rng.shuffle(row)
+                idx[g, qst[s] + i, :len(row)] = row
+                sets[(s, t, g)] = sorted(fixed | set(pick))
+    q, k, v, dout = to_dev(Q), to_dev(inp.k), to_dev(inp.v), to_dev(dO)
+    it = torch.from_numpy(idx).cuda()
+    scale = 1 / math.sqrt(128)
+    args = (i32(qst), i32(qlens), i32(kst), i32(klens), 3, max(qlens), max(klens))
+    out = torch.empty_like(q)
+    lse = torch.empty((h_q, len(qrows)), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(1, B.attn_workspace(h_q, h_kv, 3, max(qlens), max(klens), len(qrows),
+                                             n_sel=idx.shape[-1], n_init=p.n_init,
+                                             n_local=p.n_local)), dtype=torch.uint8, device="cuda")
+    B.sparse_attn(q, k, v, *args, it, p.n_init, p.n_local, scale, out, lse, ws)
+    wsb = torch.empty(B.attn_bwd_workspace(h_q, h_kv, 3, max(qlens), max(klens), len(qrows),
+                                           k.shape[0], n_sel=idx.shape[-1], n_init=p.n_init,
+                                           n_local=p.n_local), dtype=torch.uint8, device="cuda")
+    dq = torch.full_like(q, 7.0)
+    dk = torch.full_like(k, 7.0)
+    dv = torch.full_like(v, 7.0)
+    B.sparse_attn_bwd(q, k, v, out, lse, dout, *args, it, p.n_init, p.n_local, scale, dq, dk, dv, wsb)
+    torch.cuda.synchronize()
+    dqf, dkf, dvf = to_f64(dq), to_f64(dk), to_f64(dv)
+    G = h_q // h_kv
+    for s in (0, 2):
+        ks = slice(kst[s], kst[s] + klens[s])
+        qs = slice(qst[s], qst[s] + qlens[s])
+        idx_by_pos = {klens[s] - qlens[s] + i: [sets[(s, klens[s] - qlens[s] + i, g)] for g in range(h_kv)]
+                      for i in range(qlens[s])}
+        rq, rk, rv = R.attention_grad(Q[qs], inp.k[ks], inp.v[ks], dO[qs], G, p, idx_by_pos)
+        for name, got, ref in (("dq", dqf[qs], rq), ("dk", dkf[ks], rk), ("dv", dvf[ks], rv)):
+            mr, rr = grad_errors(got, ref)
+            say(f"  seq {s} {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+            assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (s, name, mr, rr)

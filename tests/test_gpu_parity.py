@@ -149,6 +149,7 @@ def _random_lists(lengths, h_kv, p: R.Params, seed):
     ([3000, 700], 32, 2, (1, 4, 11)),
     ([2500], 32, 2, (0, 0, 9)),       # generic lists: the query's own block may or may not appear
     ([1000, 37], 16, 2, (2, 3, 5)),
+    ([1700], 8, 2, (1, 2, 6)),        # G = 4
 ])
 def test_sparse_attention_given_lists(lib, lengths, h_q, h_kv, sel):
     say(f"sparse_attn lists lengths={lengths} h_q={h_q} h_kv={h_kv} sel={sel}")
