@@ -260,7 +260,11 @@ struct Attn {
   // whose bit is set in sel.  The V^T loads are in flight during the softmax.
   __device__ __forceinline__ void consume(uint32_t sel, const uint8_t* lk, const uint8_t* lv, int b) {
     floatx4 sacc[kTPW][4];
+    // MFMA stretches run at raised wave priority, so the other wave on the
+    // SIMD fills the gaps with its softmax work rather than competing.
+    __builtin_amdgcn_s_setprio(1);
     scores(sel, lk, sacc);
+    __builtin_amdgcn_s_setprio(0);
     bf16x8 vf[8][2];
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
@@ -270,6 +274,7 @@ struct Attn {
 #pragma unroll
     for (int k = 0; k < kTPW; ++k)
       if ((sel >> k) & 1u) softmax_block(k, b, sacc[k], pb[k]);
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < kTPW; ++k) {
       if (!((sel >> k) & 1u)) continue;
@@ -278,6 +283,7 @@ struct Attn {
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) o[k][dt] = mfma16(vf[dt][kk], pb[k][kk], o[k][dt]);
     }
+    __builtin_amdgcn_s_setprio(0);
   }
 
   // Private phase: this wave alone stages K block b into its LDS region
@@ -320,6 +326,7 @@ struct Attn {
     for (int k = 0; k < kTPW; ++k) {
       if (!((sel >> k) & 1u)) continue;
       floatx4 sacc[4];
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         bf16x8 kf[4];
@@ -329,12 +336,15 @@ struct Attn {
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) sacc[kt] = mfma16(kf[ks], qb[k][ks], sacc[kt]);
       }
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 pb[2];
       softmax_block(k, b, sacc, pb);
+      __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) o[k][dt] = mfma16(as_bf16x8(vb[dt][kk]), pb[kk], o[k][dt]);
+      __builtin_amdgcn_s_setprio(0);
     }
   }
 
