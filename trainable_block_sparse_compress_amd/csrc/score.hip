@@ -135,15 +135,17 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
       qa[k][ks] = as_bf16x8(v);
     }
     if (PASS == 2) {
+      // Loads at clamped addresses first, the conditions after, so the four
+      // loads are in flight together.
+      float lraw[4];
+      const int64_t lrow = min(trow[k], a.rows_q - 1);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        lraw[r] = a.lse[(int64_t)(g * a.G + min(4 * q4 + r, a.G - 1)) * a.rows_q + lrow];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int head = 4 * q4 + r;
-        float L = __builtin_inff();
-        if (need[k] && head < a.G) {
-          const float l = a.lse[(int64_t)(g * a.G + head) * a.rows_q + trow[k]];
-          if (l > -__builtin_inff()) L = l * 1.4426950408889634f;
-        }
-        Lc[k][r] = L;
+        const bool use = need[k] && 4 * q4 + r < a.G && lraw[r] > -__builtin_inff();
+        Lc[k][r] = use ? lraw[r] * 1.4426950408889634f : __builtin_inff();
       }
     }
   }
