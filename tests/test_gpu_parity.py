@@ -345,6 +345,32 @@ def _e2e(inp, lengths, h_q, h_kv, p: R.Params, positions_by_seq, check_sel=True)
     return plan, out
 
 
+@pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_select_flat_scores_lowest_index(lib, mode):
+    """Zero queries make every block score of a row equal, so the top-k is
+    the n_topk lowest candidate blocks (ties go to the lower block index).
+    At n = 40960 rows have up to 607 candidates, more than the top-k kernel
+    keeps in its compacted LDS list, so both of its paths run."""
+    say(f"select flat scores {mode}")
+    n, h_q, h_kv = 40960, 32, 2
+    p = R.Params(n_init=1, n_local=32, n_topk=63, lse_mode=mode)
+    inp = D.make_prefill(5, [n], h_q, h_kv)
+    inp.q[...] = 0
+    _, idx, _ = _run_select(inp, [n], h_q, h_kv, p)
+    n_sel = p.n_init + p.n_local + p.n_topk
+    bt = np.arange(n) // 64
+    want = np.full((n, n_sel), -1, dtype=np.int64)
+    e = np.arange(n_sel)
+    few = bt - p.n_local - p.n_init + 1 <= p.n_topk        # every causal block
+    want[few] = np.where(e[None, :] <= bt[few, None], e[None, :], -1)
+    many = ~few
+    want[many, :p.n_init + p.n_topk] = np.arange(p.n_init + p.n_topk)[None, :]
+    want[many, p.n_init + p.n_topk:] = bt[many, None] - p.n_local + 1 + np.arange(p.n_local)[None, :]
+    for g in range(h_kv):
+        bad = np.nonzero((idx[g].astype(np.int64) != want).any(axis=1))[0]
+        assert bad.size == 0, (g, bad[:5], idx[g, bad[:1]], want[bad[:1]])
+
+
 def test_tiny_full_budget_equals_dense(lib):
     """|I| = 64 covers all 64 blocks of n = 4096: the sparse path must equal
     dense causal attention (oracle dense and the GPU dense kernel)."""
