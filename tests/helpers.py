@@ -27,9 +27,11 @@ def check_selection(gpu_blocks, oracle_blocks, info, t, p, rel=REL_TIE):
     cands = info["cands"]
     if len(cands) <= p.n_topk:
         return sorted(g) == sorted(oracle_blocks), False, 0
+    k = p.n_topk
+    if k == 0:                       # no top-k: exactly the init and local blocks
+        return set(g) == fixed and sorted(g) == sorted(oracle_blocks), False, 0
     scores = info["scores"]          # oracle candidate scores in oracle order (desc, idx asc)
     order = info["order"]
-    k = p.n_topk
     sk, sk1 = scores[k - 1], scores[k]
     exempt = (sk - sk1) < rel * sk
     gsel = set(g) - fixed

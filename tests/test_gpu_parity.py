@@ -312,6 +312,21 @@ def test_select_group16_ragged(lib, mode):
     say(f"  {stats}")
 
 
+@pytest.mark.parametrize("sel", [(0, 2, 9), (2, 0, 7), (1, 3, 0), (1, 2, 80), (0, 0, 64)])
+def test_select_budgets(lib, sel):
+    """Unusual budgets: no init, no local or no top-k blocks, and top-k
+    counts at and above 64 (the top-k kernel's lane-maximum bound applies
+    only up to 64), 8q/2kv, two ragged sequences, sampled rows."""
+    say(f"select budgets {sel}")
+    lengths, h_q, h_kv = [12000, 7001], 8, 2
+    p = R.Params(n_init=sel[0], n_local=sel[1], n_topk=sel[2], lse_mode="exact")
+    inp = D.make_prefill(8, lengths, h_q, h_kv, n_needles=3)
+    _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
+    pos = [sample_positions(n, 40, seed=10 + s) for s, n in enumerate(lengths)]
+    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos)
+    say(f"  {stats}")
+
+
 # ----------------------------------------------------------------------------
 # end-to-end sparse path
 # ----------------------------------------------------------------------------

@@ -132,6 +132,12 @@ __global__ __launch_bounds__(256) void topk_kernel(TopkArgs a) {
     for (int e = lane; e < n_sel; e += 64) out[e] = e <= bt ? e : -1;
     return;
   }
+  if (a.n_topk == 0) {
+    // No top-k: the init and local blocks only.
+    for (int e = lane; e < a.n_init; e += 64) out[e] = e;
+    for (int r = lane; r < a.n_local; r += 64) out[a.n_init + r] = bt - a.n_local + 1 + r;
+    return;
+  }
 
   const float* row_bs = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld + lo;
   uint32_t key[PER];
@@ -312,6 +318,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(TopkArgs a) {
   const int nc = hi - lo + 1;
   if (nc <= a.n_topk) {
     for (int e = tid; e < n_sel; e += kRowThreads) out[e] = e <= bt ? e : -1;
+    return;
+  }
+  if (a.n_topk == 0) {
+    for (int e = tid; e < a.n_init; e += kRowThreads) out[e] = e;
+    for (int r = tid; r < a.n_local; r += kRowThreads) out[a.n_init + r] = bt - a.n_local + 1 + r;
     return;
   }
   const float* row_bs = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld + lo;
