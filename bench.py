@@ -67,7 +67,8 @@ def source_hash(path):
 
 def traffic_from_profile(kernel_src):
     """HBM bytes per launch from the committed PMC summary, if it was taken
-    on the current kernel source; None otherwise."""
+    on the current kernel source; None otherwise.  The summary covers the
+    default workload (n = 131072, exact LSE) only."""
     f = os.path.join(ROOT, "profiles", "attn_kernel_128k_pmc.json")
     if not os.path.exists(f):
         return None
@@ -216,7 +217,7 @@ def main():
     mfma_flops = w["attn_flops"] + lse_flops + w["blocks_flops"]
     attn_tflops = w["attn_flops"] / (ms_attn * 1e-3) / 1e12
     kernel_src = os.path.join(ROOT, "trainable_block_sparse_compress_amd", "csrc", "attention.hip")
-    traffic = traffic_from_profile(kernel_src)
+    traffic = traffic_from_profile(kernel_src) if (n == 131072 and args.lse == "exact") else None
     res = {
         "metric": METRIC,
         "value": n / (ms * 1e-3),
