@@ -64,6 +64,8 @@ struct AttnLds {
   int32_t ub[kWin];             // compacted shared-phase (block, mask) list
   uint32_t um[kWin];
   int32_t cnt[kWin / kThreads][kAttnWaves];
+  int32_t pcnt[kTileTok];       // private blocks per tile token
+  int32_t perm[kTileTok];       // token (tile index) of each wave slot 2w + k
 };
 static_assert(kRing * 2 * 64 * 256 == kAttnWaves * 64 * 256, "private regions alias the ring");
 
@@ -81,6 +83,41 @@ struct Attn {
   bf16x8 qb[kTPW][4];
   floatx4 o[kTPW][8];
   float m[kTPW], l[kTPW];
+  int tb[kTPW];                 // tile-token index (mask bit) of each of the wave's tokens
+
+  // Mask bits of this wave's tokens, gathered into bits 0 .. kTPW-1.
+  __device__ __forceinline__ uint32_t sel_of(uint32_t v) const {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k) r |= ((v >> tb[k]) & 1u) << k;
+    return r;
+  }
+  __device__ __forceinline__ uint32_t mine_mask() const {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < kTPW; ++k) r |= 1u << tb[k];
+    return r;
+  }
+  // State of token k of this wave: tile token tt (query row i0 + tt).
+  __device__ __forceinline__ void init_token(int k, int tt, int i0, int pos0) {
+    tb[k] = tt;
+    const int i = i0 + tt;
+    tpos[k] = pos0 + i;
+    trow[k] = (int64_t)rq.start + i;
+    tval[k] = i < rq.len && trow[k] < a.rows_q && tpos[k] >= 0;
+    bt[k] = tval[k] ? tpos[k] / kBlock : -1;
+    const bool hv = tval[k] && c16 < a.G;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = zero16();
+      if (hv) v = ldg16(a.q + (trow[k] * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
+      qb[k][ks] = as_bf16x8(v);
+    }
+    m[k] = -1e30f;
+    l[k] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) o[k][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   __device__ Attn(const AttnArgs& args) : a(args) {}
 
@@ -349,13 +386,15 @@ struct Attn {
   }
 
   // One window of blocks [w0, w1): build the token masks, run the shared
-  // phase over the popular blocks, then the private phase.  kPair: balance
-  // the shared list (left out of the multi-window kernel, whose loop leaves
-  // no registers for it).
-  template <bool kPair>
+  // phase over the popular blocks, then the private phase.  kSingle: the
+  // single-window kernel, which also balances the tokens over the waves and
+  // orders the shared list (both left out of the multi-window kernel, whose
+  // loop keeps every token on its wave and leaves no registers to spare).
+  template <bool kSingle>
   __device__ __forceinline__ void window(AttnLds& sh, int w0, int w1, int nq, int pos0, int i0,
                                          bool dense, int tid) {
     // 1. init / local (dense: every causal block), by arithmetic.
+    if (tid < kTileTok) sh.pcnt[tid] = 0;
     for (int b = w0 + tid; b < w1; b += kThreads) {
       uint32_t msk = 0;
       // (a block past the V^T row would mean inconsistent lengths: skipped)
@@ -376,7 +415,7 @@ struct Attn {
       for (int k = 0; k < kTPW; ++k) {
         if (!tval[k]) continue;
         const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + trow[k]) * a.n_sel;
-        const uint32_t bit = 1u << (wave * kTPW + k);
+        const uint32_t bit = 1u << tb[k];
         for (int e = lane; e < a.n_sel; e += 64) {
           const int b = list[e];
           if (b >= 0 && b <= bt[k] && b >= w0 && b < w1 && kBlock * b + kBlock <= a.vt_ld)
@@ -395,6 +434,9 @@ struct Attn {
       const int e = kThreads * j + tid;
       const uint32_t v = e < nblk ? sh.mask[e] : 0u;
       bal[j] = __ballot(v != 0u && (dense || __builtin_popcount(v) >= kShareMin));
+      if (kSingle && !dense && v != 0u && __builtin_popcount(v) < kShareMin) {
+        for (uint32_t x = v; x != 0u; x &= x - 1u) atomicAdd(&sh.pcnt[__builtin_ctz(x)], 1);
+      }
       if (lane == 0) sh.cnt[j][wave] = __builtin_popcountll(bal[j]);
     }
     __syncthreads();
@@ -418,12 +460,34 @@ struct Attn {
       n_ent += total;
     }
     __syncthreads();
+    // 3a. balance the private phase: the tokens ranked by private block
+    //     count are paired heaviest with lightest, one pair per wave, and the
+    //     waves take over their new tokens (no token has been touched yet).
+    if (kSingle && !dense) {
+      if (wave == 0 && lane < kTileTok) {
+        const int c = sh.pcnt[lane];
+        int rank = 0;
+#pragma unroll
+        for (int j = 0; j < kTileTok; ++j) {
+          const int cj = sh.pcnt[j];
+          rank += (cj > c || (cj == c && j < lane)) ? 1 : 0;
+        }
+        const int slot = rank < kTileTok / 2 ? kTPW * rank : kTPW * (kTileTok - 1 - rank) + 1;
+        sh.perm[slot] = lane;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k) {
+        const int tt = __builtin_amdgcn_readfirstlane(sh.perm[wave * kTPW + k]);
+        if (tt != tb[k]) init_token(k, tt, i0, pos0);
+      }
+    }
     // 3b. order the shared list for balance: within each run of 64 entries an
     //     entry is followed by the first later one whose tokens lie in other
     //     waves (else by the next one), so the two blocks of a batch tend to
     //     occupy different waves.  Runs are 64 entries, so batches of two
     //     never straddle them.
-    if (kPair && !dense) {
+    if (kSingle && !dense) {
       for (int c = wave; 64 * c < n_ent; c += kAttnWaves) {
         const int cnt = min(64, n_ent - 64 * c);
         const bool ok = lane < cnt;
@@ -431,8 +495,12 @@ struct Attn {
         const uint32_t umv = ok ? sh.um[64 * c + lane] : 0u;
         uint32_t wm = 0;
 #pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w)
-          wm |= (uint32_t)(((umv >> (kTPW * w)) & ((1u << kTPW) - 1u)) != 0u) << w;
+        for (int w = 0; w < kAttnWaves; ++w) {
+          uint32_t wb = 0;
+#pragma unroll
+          for (int k = 0; k < kTPW; ++k) wb |= 1u << sh.perm[kTPW * w + k];
+          wm |= (uint32_t)((umv & wb) != 0u) << w;
+        }
         const uint64_t valid = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
         uint64_t used = 0;
         int dest = 0, p = 0;
@@ -482,11 +550,10 @@ struct Attn {
         }
         if (u + 2 < n_ent) stage_issue(sh.ring[2 * (half ^ 1)][0], sh.ring[2 * (half ^ 1)][1], sh.ub[u + 2]);
         if (u + 3 < n_ent) stage_issue(sh.ring[2 * (half ^ 1) + 1][0], sh.ring[2 * (half ^ 1) + 1][1], sh.ub[u + 3]);
-        const uint32_t sh_mask = (1u << kTPW) - 1u;
-        const uint32_t m0 = (__builtin_amdgcn_readfirstlane(sh.um[u]) >> (wave * kTPW)) & sh_mask;
+        const uint32_t m0 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u]));
         if (m0) consume(m0, sh.ring[2 * half][0], sh.ring[2 * half][1], b0);
         if (b1 >= 0) {
-          const uint32_t m1 = (__builtin_amdgcn_readfirstlane(sh.um[u + 1]) >> (wave * kTPW)) & sh_mask;
+          const uint32_t m1 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u + 1]));
           if (m1) consume(m1, sh.ring[2 * half + 1][0], sh.ring[2 * half + 1][1], b1);
         }
       }
@@ -498,7 +565,7 @@ struct Attn {
     //    in registers) while the previous one computes.
     if (!dense) {
       uint8_t* region = &sh.ring[0][0][0] + wave * (64 * 256);
-      const uint32_t mine = ((1u << kTPW) - 1u) << (wave * kTPW);
+      const uint32_t mine = mine_mask();
       int chunk = 0;
       uint64_t pend = 0;
       // Next private block of this wave (wave-uniform), or -1.
@@ -512,7 +579,7 @@ struct Attn {
         }
         const int e = (chunk - 1) * 64 + (int)__builtin_ctzll(pend);
         pend &= pend - 1;
-        sel = (__builtin_amdgcn_readfirstlane(sh.mask[e]) >> (wave * kTPW)) & ((1u << kTPW) - 1u);
+        sel = sel_of(__builtin_amdgcn_readfirstlane(sh.mask[e]));
         return w0 + e;
       };
       uint32_t sc = 0;
@@ -566,24 +633,7 @@ struct Attn {
     init_offsets();
 
 #pragma unroll
-    for (int k = 0; k < kTPW; ++k) {
-      const int i = i0 + wave * kTPW + k;
-      tpos[k] = pos0 + i;
-      trow[k] = (int64_t)rq.start + i;
-      tval[k] = i < rq.len && trow[k] < a.rows_q && tpos[k] >= 0;
-      bt[k] = tval[k] ? tpos[k] / kBlock : -1;
-      const bool hv = tval[k] && c16 < a.G;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 v = zero16();
-        if (hv) v = ldg16(a.q + (trow[k] * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
-        qb[k][ks] = as_bf16x8(v);
-      }
-      m[k] = -1e30f;
-      l[k] = 0.f;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) o[k][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int k = 0; k < kTPW; ++k) init_token(k, wave * kTPW + k, i0, pos0);
 
     const int nq = min(kTileTok, rq.len - i0);
     const int bt_last = max(0, pos0 + i0 + nq - 1) / kBlock;
