@@ -18,7 +18,9 @@
 //  - Private phase: blocks attended by few tokens are streamed by the waves
 //    that own those tokens, each on its own (K through a per-wave LDS region,
 //    V^T straight into registers), with no workgroup barrier, so a wave that
-//    owns many private blocks does not hold up the others.
+//    owns many private blocks does not hold up the others.  Tokens are
+//    assigned to waves only once the masks are known, heaviest private load
+//    paired with lightest, so the waves' private phases end together.
 // The 16 heads of the group form the 16-wide MFMA tile.
 // Products are computed transposed: S^T = K Q^T (16 keys x 16 heads per
 // MFMA), then O^T += V^T P^T.  With the key order chosen below, the S^T
