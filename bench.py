@@ -146,8 +146,8 @@ def main():
                     help="sweep: selection sizes |I| (1 init block, |I|//3 local, rest top-k)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus must be 1 "
-                                   "(multi-GPU sharding is described in DESIGN.md, not built)"}))
+        print(json.dumps({"error": "the library runs on one GPU; --gpus must be 1 "
+                                   "(sharding across GPUs is not implemented)"}))
         sys.exit(2)
 
     if args.workload == "decode":
