@@ -736,6 +736,44 @@ struct Dq {
         n_ent += total;
       }
       __syncthreads();
+      // Order the list for balance: within each run of 64 entries an entry
+      // is followed by the first later one whose rows lie in other waves
+      // (else by the next one), so the two blocks of a batch tend to occupy
+      // different waves.  Runs are 64 entries, so batches never straddle them.
+      for (int c = wave; 64 * c < n_ent; c += kDqWaves) {
+        const int cnt = min(64, n_ent - 64 * c);
+        const bool ok = lane < cnt;
+        const int32_t ubv = ok ? sh.ub[64 * c + lane] : 0;
+        const uint32_t umv = ok ? sh.um[64 * c + lane] : 0u;
+        uint32_t wm = 0;
+#pragma unroll
+        for (int w = 0; w < kDqWaves; ++w)
+          wm |= (uint32_t)(((umv >> (kDqTPW * w)) & ((1u << kDqTPW) - 1u)) != 0u) << w;
+        const uint64_t valid = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
+        uint64_t used = 0;
+        int dest = 0, p = 0;
+        for (int i = 0; i < cnt; ++i) {
+          if ((used >> i) & 1ull) continue;
+          used |= 1ull << i;
+          dest = lane == i ? p : dest;
+          ++p;
+          const uint32_t aw = __builtin_amdgcn_readlane(wm, i);
+          const uint64_t later = valid & ~used & ~((2ull << i) - 1ull);
+          uint64_t cand = __ballot((wm & aw) == 0u) & later;
+          if (cand == 0) cand = later;
+          if (cand != 0) {
+            const int j = (int)__builtin_ctzll(cand);
+            used |= 1ull << j;
+            dest = lane == j ? p : dest;
+            ++p;
+          }
+        }
+        if (ok) {
+          sh.ub[64 * c + dest] = ubv;
+          sh.um[64 * c + dest] = umv;
+        }
+      }
+      __syncthreads();
       if (n_ent > 0) {
         stage_issue(sh.ring[0][0], sh.ring[0][1], sh.ub[0]);
         if (n_ent > 1) stage_issue(sh.ring[1][0], sh.ring[1][1], sh.ub[1]);
