@@ -218,6 +218,48 @@ def test_backward_full_size_sampled(lib, n):
         assert dv_err.max() <= 1e-2 and dk_err.max() <= 1e-2, (g, dv_err.max(), dk_err.max())
 
 
+def test_backward_beyond_one_window(lib):
+    """A sequence of more than 2048 blocks (the dQ kernel's loop over block
+    windows, with every block in its shared phase), 4q/1kv, |I| = 1 + 32 +
+    63: dq at sampled rows on both sides of the window edge and the last two
+    blocks' dK / dV against the oracle."""
+    n, h_q, h_kv = 133000, 4, 1
+    say(f"backward beyond one window n={n}")
+    G = h_q // h_kv
+    p = R.Params()
+    inp = D.make_prefill(50, n, h_q, h_kv, n_needles=8)
+    dO = D.make_grad(51, n, h_q)
+    idx_np = _headline_lists(n, h_kv, p, seed=52)
+    q, k, v, dout = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v), to_dev(dO)
+    dq, dk, dv = _run(q, k, v, [n], torch.from_numpy(idx_np).cuda(), p, False, dout)
+    Kf, Vf = R.as_f64(inp.k), R.as_f64(inp.v)
+
+    def blocks_of(t):
+        bt = t // 64
+        fixed = set(range(min(p.n_init, bt + 1))) | set(range(max(0, bt - p.n_local + 1), bt + 1))
+        return [sorted(fixed | {int(b) for b in idx_np[g, t] if 0 <= b <= bt}) for g in range(h_kv)]
+
+    rows = sample_positions(n, 20, seed=53, must=(131071, 131072, 131135, 131136))
+    ref = np.stack([R.attend_token_grad(inp.q[t], dO[t], t, Kf, Vf, blocks_of(t), G, p)[0]
+                    for t in rows])
+    mr, rr = grad_errors(dq[rows], ref)
+    say(f"  dq at {len(rows)} sampled rows: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+    assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (mr, rr)
+    b0 = (n - 1) // 64 - 1
+    rk = np.zeros((n - 64 * b0, h_kv, 128))
+    rv = np.zeros((n - 64 * b0, h_kv, 128))
+    for t in range(64 * b0, n):
+        _, parts = R.attend_token_grad(inp.q[t], dO[t], t, Kf, Vf, blocks_of(t), G, p)
+        for g, (u, gk, gv) in enumerate(parts):
+            m = u >= 64 * b0
+            rk[u[m] - 64 * b0, g] += gk[m]
+            rv[u[m] - 64 * b0, g] += gv[m]
+    for name, got, ref in (("dk", dk[64 * b0:], rk), ("dv", dv[64 * b0:], rv)):
+        mr, rr = grad_errors(got, ref)
+        say(f"  tail blocks {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+        assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (name, mr, rr)
+
+
 def test_autograd_switch_matches_direct_calls(lib):
     """attention_trainable: torch autograd through the switch (one dense and
     one sparse sequence) gives exactly the gradients of the direct backward

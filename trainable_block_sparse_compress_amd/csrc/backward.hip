@@ -473,9 +473,13 @@ constexpr int kDqTPW = 2;
 constexpr int kDqThreads = 64 * kDqWaves;
 constexpr int kDqWin = 2048;
 constexpr int kDqRing = 4;
+constexpr int kDqShareMin = 2;   // rows of the tile attending a block for the shared phase
 
 struct DqLds {
-  uint8_t ring[kDqRing][2][64 * 256];   // slot: K block, V block
+  // Shared phase: slot r holds a K block at ring[r][0] and its V at
+  // ring[r][1].  Private phase: wave w owns the 16 KB at (ring[0][0] +
+  // 16 KB * w) for the K block it is streaming.
+  uint8_t ring[kDqRing][2][64 * 256];
   uint32_t mask[kDqWin];
   int32_t ub[kDqWin];
   uint32_t um[kDqWin];
@@ -597,6 +601,109 @@ struct Dq {
     return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
   }
 
+  // Private phase: this wave alone stages K block b into its LDS region
+  // (16 direct global->LDS loads of 1 KB, the shared phase's layout).
+  __device__ __forceinline__ void issue_k_private(uint8_t* lk, int b) const {
+    if (k_inside(b)) {
+      const int lo0 = opaque(klo[0]), lo1 = opaque(klo[1]);
+      const uint16_t* bk = kbase + (int64_t)(kBlock * b) * krow;
+#pragma unroll
+      for (int part = 0; part < 16; ++part)
+        __builtin_amdgcn_global_load_lds(bk + (int64_t)(4 * part) * krow + ((part & 2) ? lo1 : lo0),
+                                         (__attribute__((address_space(3))) void*)(lk + part * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int part = 0; part < 16; ++part) stage_part_clamped(lk, a.k, b, part);
+    }
+  }
+  // Private phase: the V fragments of block b straight into registers, in
+  // the A-operand layout the shared phase reads from LDS (fragment (kt, ks):
+  // key row key0 + 32 (kt / 2) + 4 (kt % 2), dims 32 ks + 8 q4 .. +8), rows
+  // clamped to the tensor.
+  __device__ __forceinline__ void load_v_private(u32x4 (&vb)[4][4], int b) const {
+    const int key0 = 8 * (c16 >> 2) + (c16 & 3);
+    if (k_inside(b)) {
+      const uint16_t* p = vbase + (int64_t)(kBlock * b + key0) * krow + 8 * q4;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          vb[kt][ks] = ldg16(p + (int64_t)(32 * (kt >> 1) + 4 * (kt & 1)) * krow + 32 * ks);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        int64_t r = (int64_t)rk.start + kBlock * b + key0 + 32 * (kt >> 1) + 4 * (kt & 1);
+        r = r < a.rows_k ? r : a.rows_k - 1;
+        const uint16_t* p = a.v + (r * a.h_kv + g) * kHeadDim + 8 * q4;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) vb[kt][ks] = ldg16(p + 32 * ks);
+      }
+    }
+  }
+  // Zero this wave's staged K rows at or past the sequence end (see zero_tail).
+  __device__ __forceinline__ void zero_tail_private(uint8_t* lk, int b) const {
+    const int first = rk.len - kBlock * b;
+    for (int c = lane; c < 64 * 16; c += 64) {
+      const int row = c >> 4;
+      if (row >= first) *reinterpret_cast<u32x4*>(lk + row * 256 + ((c & 15) << 4)) = zero16();
+    }
+  }
+
+  // Private phase, block b for the rows of this wave in sel: K from the
+  // wave's region, V from registers.
+  __device__ __forceinline__ void consume_private(uint32_t sel, const uint8_t* lk, const u32x4 (&vb)[4][4], int b) {
+#pragma unroll
+    for (int k = 0; k < kDqTPW; ++k) {
+      if (!((sel >> k) & 1u)) continue;
+      const bool diag = b == bt[k];
+      const int lim = tpos[k] - kBlock * b - 8 * q4;
+      bf16x8 dsb[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        float ds[2][4];
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kt = 2 * kk + half;
+          const int roff = 256 * (32 * (kt >> 1) + 4 * (kt & 1));
+          floatx4 st = floatx4{0.f, 0.f, 0.f, 0.f}, dp = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            st = mfma16(lds16(lk + koff[ks] + roff), qb[k][ks], st);
+            dp = mfma16(as_bf16x8(vb[kt][ks]), db[k][ks], dp);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const bool vis = !diag || 32 * (kt >> 1) + 4 * (kt & 1) + r <= lim;
+            const float pr = fast_exp2(fmaf(st[r], a.c, -l2[k]));
+            ds[half][r] = vis ? pr * (dp[r] - dd[k]) : 0.f;
+          }
+        }
+        u32x4 w;
+        w[0] = pack_bf16x2(ds[0][0], ds[0][1]);
+        w[1] = pack_bf16x2(ds[0][2], ds[0][3]);
+        w[2] = pack_bf16x2(ds[1][0], ds[1][1]);
+        w[3] = pack_bf16x2(ds[1][2], ds[1][3]);
+        dsb[kk] = as_bf16x8(w);
+      }
+      auto step = [&](auto dtc, auto kkc) {
+        constexpr int dt = decltype(dtc)::value, kk = decltype(kkc)::value;
+        acc[k][dt] = mfma16(kt_frag<dt, kk>(lk), dsb[kk], acc[k][dt]);
+      };
+      auto dts = [&](auto kkc) {
+        step(std::integral_constant<int, 0>{}, kkc);
+        step(std::integral_constant<int, 1>{}, kkc);
+        step(std::integral_constant<int, 2>{}, kkc);
+        step(std::integral_constant<int, 3>{}, kkc);
+        step(std::integral_constant<int, 4>{}, kkc);
+        step(std::integral_constant<int, 5>{}, kkc);
+        step(std::integral_constant<int, 6>{}, kkc);
+        step(std::integral_constant<int, 7>{}, kkc);
+      };
+      dts(std::integral_constant<int, 0>{});
+      dts(std::integral_constant<int, 1>{});
+    }
+  }
+
   // Block b (K at lk, V at lv) for the rows of this wave in sel.
   __device__ __forceinline__ void consume(uint32_t sel, const uint8_t* lk, const uint8_t* lv, int b) {
     bf16x8 dsb[kDqTPW][2];
@@ -655,6 +762,10 @@ struct Dq {
     dts(std::integral_constant<int, 1>{});
   }
 
+  // kMulti: keys beyond one window of kDqWin blocks; that instance loops over
+  // windows and keeps every block in the shared phase (a loop around both
+  // phases would keep their registers live at once).
+  template <bool kMulti>
   __device__ void run(DqLds& sh) {
     const int tile = blockIdx.x;
     g = blockIdx.y;
@@ -702,7 +813,8 @@ struct Dq {
     const int nq = min(16, rq.len - i0);
     const int bt_last = min(max(0, pos0 + i0 + nq - 1) / kBlock, a.nblk - 1);
     const uint16_t* mrow = a.mask_t + (((int64_t)g * a.batch + s) * a.ntiles + tile) * a.nblk;
-    for (int w0 = 0; w0 <= bt_last; w0 += kDqWin) {
+    const int w_last = kMulti ? bt_last : 0;
+    for (int w0 = 0; w0 <= w_last; w0 += kDqWin) {
       const int w1 = min(bt_last + 1, w0 + kDqWin);
       const int nblk = w1 - w0;
       for (int e = tid; e < kDqWin; e += kDqThreads) sh.mask[e] = e < nblk ? mrow[w0 + e] : 0u;
@@ -712,7 +824,8 @@ struct Dq {
 #pragma unroll
       for (int j = 0; j < kDqWin / kDqThreads; ++j) {
         const int e = kDqThreads * j + tid;
-        bal[j] = __ballot(sh.mask[e] != 0u);
+        const uint32_t v = sh.mask[e];
+        bal[j] = __ballot(v != 0u && (kMulti || __builtin_popcount(v) >= kDqShareMin));
         if (lane == 0) sh.cnt[j][wave] = __builtin_popcountll(bal[j]);
       }
       __syncthreads();
@@ -802,6 +915,51 @@ struct Dq {
         }
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       }
+      // Private phase: this wave's blocks that stayed out of the shared list,
+      // ascending, one block in flight (K in the wave's region, V in
+      // registers) while the previous one computes.
+      if constexpr (!kMulti) {
+        __syncthreads();   // the ring becomes the private regions
+        uint8_t* region = &sh.ring[0][0][0] + wave * (64 * 256);
+        const uint32_t mine = ((1u << kDqTPW) - 1u) << (wave * kDqTPW);
+        int chunk = 0;
+        uint64_t pend = 0;
+        // Next private block of this wave (wave-uniform), or -1.
+        auto next_block = [&](uint32_t& sel) -> int {
+          while (pend == 0) {
+            if (chunk * 64 >= nblk) return -1;
+            const int e = chunk * 64 + lane;
+            const uint32_t v = e < nblk ? sh.mask[e] : 0u;
+            pend = __ballot((v & mine) != 0u && __builtin_popcount(v) < kDqShareMin);
+            ++chunk;
+          }
+          const int e = (chunk - 1) * 64 + (int)__builtin_ctzll(pend);
+          pend &= pend - 1;
+          sel = (__builtin_amdgcn_readfirstlane(sh.mask[e]) >> (wave * kDqTPW)) & ((1u << kDqTPW) - 1u);
+          return w0 + e;
+        };
+        uint32_t sc = 0;
+        int bc = next_block(sc);
+        u32x4 vb[4][4];
+        if (bc >= 0) {
+          issue_k_private(region, bc);
+          load_v_private(vb, bc);
+        }
+        while (bc >= 0) {
+          uint32_t sn = 0;
+          const int bn = next_block(sn);
+          __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // K(bc) in the region, V(bc) in registers
+          if (kBlock * bc + kBlock > rk.len) zero_tail_private(region, bc);
+          consume_private(sc, region, vb, bc);
+          if (bn >= 0) {
+            __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the region's K reads are done
+            issue_k_private(region, bn);
+            load_v_private(vb, bn);
+          }
+          bc = bn;
+          sc = sn;
+        }
+      }
       __syncthreads();   // the ring and the lists are reused by the next window
     }
 
@@ -820,10 +978,11 @@ struct Dq {
   }
 };
 
+template <bool kMulti>
 __global__ __launch_bounds__(kDqThreads) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) DqLds sh;
   Dq st(a);
-  st.run(sh);
+  st.run<kMulti>(sh);
 }
 
 }  // namespace
@@ -837,7 +996,11 @@ hipError_t launch_attention_bwd(const BwdArgs& a, int max_seqlen_q, int max_seql
   hipLaunchKernelGGL(bwd_count_kernel, dim3((a.nblk + 3) / 4, a.h_kv, a.batch), dim3(256), 0, st, a);
   hipLaunchKernelGGL(bwd_list_kernel, dim3(1), dim3(1024), 0, st, a);
   hipLaunchKernelGGL(bwd_dkdv_kernel, dim3(a.wmax), dim3(64 * kDkvWaves), 0, st, a);
-  hipLaunchKernelGGL(bwd_dq_kernel, dim3((max_seqlen_q + 15) / 16, a.h_kv, a.batch), dim3(kDqThreads), 0, st, a);
+  const dim3 dq_grid((max_seqlen_q + 15) / 16, a.h_kv, a.batch);
+  if (a.nblk <= kDqWin)
+    hipLaunchKernelGGL(bwd_dq_kernel<false>, dq_grid, dim3(kDqThreads), 0, st, a);
+  else
+    hipLaunchKernelGGL(bwd_dq_kernel<true>, dq_grid, dim3(kDqThreads), 0, st, a);
   hipLaunchKernelGGL(bwd_reduce_kernel, dim3((unsigned)((int64_t)a.h_kv * a.batch * a.nblk), 2), dim3(256), 0, st, a);
   return hipGetLastError();
 }
