@@ -484,6 +484,8 @@ struct DqLds {
   int32_t ub[kDqWin];
   uint32_t um[kDqWin];
   int32_t cnt[kDqWin / kDqThreads][kDqWaves];
+  int32_t pcnt[16];   // private blocks per tile row
+  int32_t perm[16];   // tile row of each wave slot 2w + k
 };
 
 struct Dq {
@@ -496,6 +498,7 @@ struct Dq {
   bf16x8 qb[kDqTPW][4], db[kDqTPW][4];
   floatx4 acc[kDqTPW][8];
   float l2[kDqTPW], dd[kDqTPW];
+  int tb[kDqTPW];     // tile row (mask bit) of each of the wave's rows
   const uint16_t* kbase;
   const uint16_t* vbase;
   int64_t krow;
@@ -504,6 +507,49 @@ struct Dq {
   int gbase[2][2];   // K^T gather: per (key parity, sign) lane base offsets
 
   __device__ Dq(const BwdArgs& args) : a(args) {}
+
+  // Mask bits of this wave's rows, gathered into bits 0 .. kDqTPW-1.
+  __device__ __forceinline__ uint32_t sel_of(uint32_t v) const {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < kDqTPW; ++k) r |= ((v >> tb[k]) & 1u) << k;
+    return r;
+  }
+  __device__ __forceinline__ uint32_t mine_mask() const {
+    uint32_t r = 0;
+#pragma unroll
+    for (int k = 0; k < kDqTPW; ++k) r |= 1u << tb[k];
+    return r;
+  }
+  // State of row k of this wave: tile row tt (query row i0 + tt).
+  __device__ __forceinline__ void init_token(int k, int tt, int i0, int pos0) {
+    tb[k] = tt;
+    const int i = i0 + tt;
+    tpos[k] = pos0 + i;
+    trow[k] = (int64_t)rq.start + i;
+    tval[k] = i < rq.len && trow[k] < a.rows_q && tpos[k] >= 0;
+    bt[k] = tval[k] ? tpos[k] / kBlock : -1;
+    const bool hv = tval[k] && c16 < a.G;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 vq = zero16(), vd = zero16();
+      if (hv) {
+        const int64_t o = (trow[k] * a.h_q + (int64_t)g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4;
+        vq = ldg16(a.q + o);
+        vd = ldg16(a.dout + o);
+      }
+      qb[k][ks] = as_bf16x8(vq);
+      db[k][ks] = as_bf16x8(vd);
+    }
+    l2[k] = __builtin_inff();
+    dd[k] = 0.f;
+    if (tval[k]) {
+      l2[k] = a.lse2[(trow[k] * a.h_kv + g) * 16 + c16];
+      dd[k] = a.dd[(trow[k] * a.h_kv + g) * 16 + c16];
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[k][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   __device__ __forceinline__ void init_offsets() {
     krow = (int64_t)a.h_kv * kHeadDim;
@@ -781,33 +827,11 @@ struct Dq {
     q4 = lane >> 4;
     c16 = lane & 15;
     init_offsets();
+    // The multi-window instance keeps row 2w + k on wave w; the single-window
+    // one assigns the rows once the masks are known (below).
+    if constexpr (kMulti) {
 #pragma unroll
-    for (int k = 0; k < kDqTPW; ++k) {
-      const int i = i0 + wave * kDqTPW + k;
-      tpos[k] = pos0 + i;
-      trow[k] = (int64_t)rq.start + i;
-      tval[k] = i < rq.len && trow[k] < a.rows_q && tpos[k] >= 0;
-      bt[k] = tval[k] ? tpos[k] / kBlock : -1;
-      const bool hv = tval[k] && c16 < a.G;
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 vq = zero16(), vd = zero16();
-        if (hv) {
-          const int64_t o = (trow[k] * a.h_q + (int64_t)g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4;
-          vq = ldg16(a.q + o);
-          vd = ldg16(a.dout + o);
-        }
-        qb[k][ks] = as_bf16x8(vq);
-        db[k][ks] = as_bf16x8(vd);
-      }
-      l2[k] = __builtin_inff();
-      dd[k] = 0.f;
-      if (tval[k]) {
-        l2[k] = a.lse2[(trow[k] * a.h_kv + g) * 16 + c16];
-        dd[k] = a.dd[(trow[k] * a.h_kv + g) * 16 + c16];
-      }
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) acc[k][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < kDqTPW; ++k) init_token(k, wave * kDqTPW + k, i0, pos0);
     }
 
     const int nq = min(16, rq.len - i0);
@@ -818,7 +842,32 @@ struct Dq {
       const int w1 = min(bt_last + 1, w0 + kDqWin);
       const int nblk = w1 - w0;
       for (int e = tid; e < kDqWin; e += kDqThreads) sh.mask[e] = e < nblk ? mrow[w0 + e] : 0u;
+      if (!kMulti && tid < 16) sh.pcnt[tid] = 0;
       __syncthreads();
+      if constexpr (!kMulti) {
+        // Balance the private phase: rows ranked by private block count are
+        // paired heaviest with lightest, one pair per wave.
+        for (int e = tid; e < nblk; e += kDqThreads) {
+          const uint32_t v = sh.mask[e];
+          if (v != 0u && __builtin_popcount(v) < kDqShareMin)
+            for (uint32_t x = v; x != 0u; x &= x - 1u) atomicAdd(&sh.pcnt[__builtin_ctz(x)], 1);
+        }
+        __syncthreads();
+        if (wave == 0 && lane < 16) {
+          const int c = sh.pcnt[lane];
+          int rank = 0;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) {
+            const int cj = sh.pcnt[j];
+            rank += (cj > c || (cj == c && j < lane)) ? 1 : 0;
+          }
+          sh.perm[rank < 8 ? kDqTPW * rank : kDqTPW * (15 - rank) + 1] = lane;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kDqTPW; ++k)
+          init_token(k, __builtin_amdgcn_readfirstlane(sh.perm[wave * kDqTPW + k]), i0, pos0);
+      }
       // Compact the attended blocks, ascending.
       uint64_t bal[kDqWin / kDqThreads];
 #pragma unroll
@@ -860,8 +909,15 @@ struct Dq {
         const uint32_t umv = ok ? sh.um[64 * c + lane] : 0u;
         uint32_t wm = 0;
 #pragma unroll
-        for (int w = 0; w < kDqWaves; ++w)
-          wm |= (uint32_t)(((umv >> (kDqTPW * w)) & ((1u << kDqTPW) - 1u)) != 0u) << w;
+        for (int w = 0; w < kDqWaves; ++w) {
+          uint32_t wb = ((1u << kDqTPW) - 1u) << (kDqTPW * w);
+          if constexpr (!kMulti) {
+            wb = 0;
+#pragma unroll
+            for (int k = 0; k < kDqTPW; ++k) wb |= 1u << sh.perm[kDqTPW * w + k];
+          }
+          wm |= (uint32_t)((umv & wb) != 0u) << w;
+        }
         const uint64_t valid = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
         uint64_t used = 0;
         int dest = 0, p = 0;
@@ -905,11 +961,10 @@ struct Dq {
           }
           if (u + 2 < n_ent) stage_issue(sh.ring[2 * (half ^ 1)][0], sh.ring[2 * (half ^ 1)][1], sh.ub[u + 2]);
           if (u + 3 < n_ent) stage_issue(sh.ring[2 * (half ^ 1) + 1][0], sh.ring[2 * (half ^ 1) + 1][1], sh.ub[u + 3]);
-          const uint32_t msk = (1u << kDqTPW) - 1u;
-          const uint32_t m0 = (__builtin_amdgcn_readfirstlane(sh.um[u]) >> (wave * kDqTPW)) & msk;
+          const uint32_t m0 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u]));
           if (m0) consume(m0, sh.ring[2 * half][0], sh.ring[2 * half][1], b0);
           if (b1 >= 0) {
-            const uint32_t m1 = (__builtin_amdgcn_readfirstlane(sh.um[u + 1]) >> (wave * kDqTPW)) & msk;
+            const uint32_t m1 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u + 1]));
             if (m1) consume(m1, sh.ring[2 * half + 1][0], sh.ring[2 * half + 1][1], b1);
           }
         }
@@ -921,7 +976,7 @@ struct Dq {
       if constexpr (!kMulti) {
         __syncthreads();   // the ring becomes the private regions
         uint8_t* region = &sh.ring[0][0][0] + wave * (64 * 256);
-        const uint32_t mine = ((1u << kDqTPW) - 1u) << (wave * kDqTPW);
+        const uint32_t mine = mine_mask();
         int chunk = 0;
         uint64_t pend = 0;
         // Next private block of this wave (wave-uniform), or -1.
@@ -935,7 +990,7 @@ struct Dq {
           }
           const int e = (chunk - 1) * 64 + (int)__builtin_ctzll(pend);
           pend &= pend - 1;
-          sel = (__builtin_amdgcn_readfirstlane(sh.mask[e]) >> (wave * kDqTPW)) & ((1u << kDqTPW) - 1u);
+          sel = sel_of(__builtin_amdgcn_readfirstlane(sh.mask[e]));
           return w0 + e;
         };
         uint32_t sc = 0;
