@@ -466,6 +466,7 @@ struct Attn {
     //     count are paired heaviest with lightest, one pair per wave, and the
     //     waves take over their new tokens (no token has been touched yet).
     if (kSingle && !dense) {
+      static_assert(kTPW == 2, "the pairing gives each wave two tokens");
       if (wave == 0 && lane < kTileTok) {
         const int c = sh.pcnt[lane];
         int rank = 0;

@@ -853,6 +853,7 @@ struct Dq {
             for (uint32_t x = v; x != 0u; x &= x - 1u) atomicAdd(&sh.pcnt[__builtin_ctz(x)], 1);
         }
         __syncthreads();
+        static_assert(kDqTPW == 2 && kDqWaves * kDqTPW == 16, "the pairing gives each wave two of 16 rows");
         if (wave == 0 && lane < 16) {
           const int c = sh.pcnt[lane];
           int rank = 0;
