@@ -468,6 +468,7 @@ __global__ __launch_bounds__(256) void bwd_reduce_kernel(BwdArgs a) {
 // where the K^T fragments (8 consecutive keys of one dim) are gathered from
 // the staged [key][dim] tile with 16-bit LDS reads.
 // ---------------------------------------------------------------------------
+typedef uint32_t uint32x2_t __attribute__((ext_vector_type(2)));
 constexpr int kDqWaves = 8;
 constexpr int kDqTPW = 2;
 constexpr int kDqThreads = 64 * kDqWaves;
@@ -504,7 +505,7 @@ struct Dq {
   int64_t krow;
   int klo[2];
   int koff[4];
-  int gbase[2][2];   // K^T gather: per (key parity, sign) lane base offsets
+  int trlb, trs2;    // K^T transposed reads: lane byte base and chunk swizzle
 
   __device__ Dq(const BwdArgs& args) : a(args) {}
 
@@ -563,25 +564,19 @@ struct Dq {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) koff[ks] = key0 * 256 + (((4 * ks + q4) ^ sw) << 4);
     // K^T fragment (dt, kk): element j is K[key 32kk + 8q4 + j][dim 16dt + c16].
-    // Its byte offset in the swizzled tile is
-    //   (32kk + 8q4 + j) * 256 + 16 * ((2dt + h) ^ ((j & 3) | 4p)) + 2 * (c16 & 7)
-    // with h = c16 / 8, p = q4 & 1, which splits into a compile-time part
-    // j*256 + 32*dt' (dt' = dt ^ ((j >> 1) & 1)) and a lane part
-    // 16 * (h ^ (j & 1)) +- 64p (sign: minus when bit 1 of dt' is set).
-    const int h = c16 >> 3, p = q4 & 1;
-    const int lb = 8 * q4 * 256 + 2 * (c16 & 7);
-#pragma unroll
-    for (int jb = 0; jb < 2; ++jb) {
-      gbase[jb][0] = lb + 16 * (h ^ jb) + 64 * p;
-      gbase[jb][1] = lb + 16 * (h ^ jb) - 64 * p;
-    }
+    // gfx950's transposed LDS read (ds_read_b64_tr_b16) hands lane i of a
+    // 16-lane group element j of the 8 bytes read by lane 4j + i/4, taken at
+    // position i % 4.  So lane L of group q4 reads the 4 dims 16dt + 4(L%4) ..
+    // +3 of key row 32kk + 8q4 + L/4 (+4 for elements 4..7); in the swizzled
+    // tile that row's chunk (2dt + (L%4)/2) sits at chunk (2dt) ^ trs2, with
+    // the row's swizzle (L/4 | 4(q4&1): the row's low bits come from L/4 and
+    // q4 alone) folded into trs2.
+    trlb = (8 * q4 + (c16 >> 2)) * 256 + 8 * (c16 & 1);
+    trs2 = ((c16 >> 2) | ((q4 & 1) << 2)) ^ ((c16 & 3) >> 1);
   }
 
   static __device__ __forceinline__ bf16x8 lds16(const uint8_t* p) {
     return as_bf16x8(*reinterpret_cast<const u32x4*>(p));
-  }
-  static __device__ __forceinline__ uint32_t lds2(const uint8_t* p) {
-    return *reinterpret_cast<const uint16_t*>(p);
   }
 
   __device__ __forceinline__ bool k_inside(int b) const {
@@ -628,23 +623,17 @@ struct Dq {
     }
   }
 
-  // K^T fragment (dt, kk) gathered from the staged K tile.
+  // K^T fragment (dt, kk) from the staged K tile: two transposed reads,
+  // keys 32kk + 8q4 + 0..3 and + 4..7 (see init_offsets).
   template <int dt, int kk>
   __device__ __forceinline__ bf16x8 kt_frag(const uint8_t* lk) const {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t x[2];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int j = 2 * i + jj;
-        const int dtp = dt ^ ((j >> 1) & 1);
-        const int sg = (dtp >> 1) & 1;
-        x[jj] = lds2(lk + gbase[j & 1][sg] + (32 * kk + j) * 256 + 32 * dtp);
-      }
-      w[i] = x[0] | (x[1] << 16);
-    }
-    return as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const uint8_t* p = lk + trlb + 16 * ((2 * dt) ^ trs2) + 8192 * kk;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 1024));
+    const uint32x2_t wl = __builtin_bit_cast(uint32x2_t, lo), wh = __builtin_bit_cast(uint32x2_t, hi);
+    return as_bf16x8(u32x4{wl[0], wl[1], wh[0], wh[1]});
   }
 
   // Private phase: this wave alone stages K block b into its LDS region
