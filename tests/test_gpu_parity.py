@@ -410,6 +410,19 @@ def test_tiny_full_budget_equals_dense(lib):
 
 
 @pytest.mark.parametrize("mode", ["exact", "approx"])
+def test_end_to_end_with_empty_sequences(lib, mode):
+    """A packed batch with empty sequences between real ones (8q/2kv,
+    |I| = 1 + 4 + 11): selection and attention of the real sequences match
+    the oracle; the empty ones own no rows."""
+    say(f"end-to-end with empty sequences {mode}")
+    lengths, h_q, h_kv = [0, 4100, 0, 1500, 0], 8, 2
+    p = R.Params(n_init=1, n_local=4, n_topk=11, lse_mode=mode)
+    inp = D.make_prefill(9, lengths, h_q, h_kv)
+    pos = [[] if n == 0 else sample_positions(n, 30, seed=20 + s) for s, n in enumerate(lengths)]
+    _e2e(inp, lengths, h_q, h_kv, p, pos)
+
+
+@pytest.mark.parametrize("mode", ["exact", "approx"])
 def test_tiny_end_to_end(lib, mode):
     say(f"tiny end-to-end {mode}")
     p = R.Params(n_init=1, n_local=4, n_topk=11, lse_mode=mode)
