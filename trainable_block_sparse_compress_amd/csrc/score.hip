@@ -19,17 +19,20 @@
 // lane ends up holding 4 heads of one window: the group sum is 3 in-lane adds
 // plus a reduce-scatter over the four 16-lane rows, after which lane l holds
 // S for window (tile start + l) and a quad max gives the block score.
-// Compressed-key tiles of 64 windows are staged in LDS (direct global->LDS
+// Compressed-key tiles of 128 windows are staged in LDS (direct global->LDS
 // loads, double-buffered: the next tile lands while this one computes) and
 // shared by the 4 waves; each LDS fragment feeds 4 MFMAs (one per token).
+// Within a tile the 16-window chunks are software-pipelined: one chunk's
+// MFMAs are in flight while the previous chunk's exponentials run.
 // Group sizes below 16 pad the head rows with zeros.
 //
 // Pass 1 keeps a per-row offset instead of a per-element running max: the
 // first 16 windows set it to their exact max; afterwards a row's sum is only
 // renormalised (by a power of two) when it exceeds 2^32, and a tile whose sum
-// overflows is redone with its exact max (both decided once per tile for the
-// whole wave).  Every exponent stays finite and the result is the same
-// log-sum-exp, with one FMA, one exp and one add per score on full tiles.
+// overflows is redone with its exact max (one test per tile for the whole
+// wave).  Every exponent stays finite and the result is the same log-sum-exp,
+// with one FMA, one exp and one add per score on full tiles; the offset is
+// kept in log2 units (scaled by scale * log2 e), so L = m ln 2 + ln(sum).
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -40,7 +43,8 @@ namespace {
 
 constexpr int kQT = 16;      // query tokens per workgroup
 constexpr int kTPW = 4;      // tokens per wave
-constexpr int kWT = 64;      // windows per tile
+constexpr int kWT = 128;     // windows per tile
+constexpr int kCT = kWT / 16;  // 16-window chunks per tile
 
 // DPP move of a float: lane i takes src from the lane the control selects;
 // lanes without a source keep `old`.
@@ -54,23 +58,37 @@ __device__ __forceinline__ int n_visible(int t, int win_kernel, int win_stride, 
   return min(nwin, (t - win_kernel + 1) / win_stride + 1);
 }
 
-// Stage kc[g, cu_c + j0 .. j0+63] into LDS with direct global->LDS loads:
-// 64 rows of 256 bytes; each wave writes 4 contiguous 1 KB parts; LDS chunk p
-// of row w receives global chunk p ^ (w & 7), so that 8 consecutive rows read
-// at the same chunk hit distinct banks.  Rows past the sequence's windows
-// read a clamped (valid) row and are masked by visibility.
-__device__ __forceinline__ void stage_windows(uint8_t* lds, const ScoreArgs& a, int g, int64_t c0,
-                                              int j0, int wave, int lane) {
+// Scheduling fence: keeps the compiler from sinking a chunk's fragment reads
+// to their first use (it does so to save registers, and the MFMAs then wait
+// on LDS latency).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Stage windows j0 .. j0 + kWT - 1 of one sequence's compressed keys into
+// LDS with direct global->LDS loads: kWT rows of 256 bytes, 1 KB parts, part
+// p written by wave p % 4.  LDS chunk c of row w receives global chunk
+// c ^ (w & 7), so that 8 consecutive rows read at the same chunk hit
+// distinct banks.  A wave's rows are 4 * wave + 16 * it + lane / 16 and its
+// chunk swizzle is the same in every part, so the per-lane byte offset
+// `voff` is loop-invariant and the tile and part advance the uniform base
+// only.  Rows past the last valid one (`rmax`, relative to the sequence's
+// first window) read that row instead and are masked by visibility.
+__device__ __forceinline__ void stage_windows(uint8_t* lds, const uint8_t* base, int j0, int rmax,
+                                              uint32_t voff, int lw, int wave) {
+  if (j0 + kWT - 1 <= rmax) {
+    const uint8_t* b = base + (int64_t)j0 * 256;
 #pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int part = wave + 4 * it;
-    const int off = part * 1024 + lane * 16;
-    const int w = off >> 8;
-    const int ch = ((off >> 4) & 15) ^ (w & 7);
-    int64_t row = c0 + j0 + w;
-    row = row < a.c_rows ? row : a.c_rows - 1;
-    __builtin_amdgcn_global_load_lds(a.kc + ((int64_t)g * a.c_rows + row) * kHeadDim + 8 * ch,
-                                     (__attribute__((address_space(3))) void*)(lds + part * 1024), 16, 0, 0);
+    for (int it = 0; it < kWT / 16; ++it)
+      __builtin_amdgcn_global_load_lds(b + it * 4096 + voff,
+                                       (__attribute__((address_space(3))) void*)(lds + (wave + 4 * it) * 1024),
+                                       16, 0, 0);
+  } else {
+#pragma unroll
+    for (int it = 0; it < kWT / 16; ++it) {
+      const int row = min(j0 + lw + 16 * it, rmax);
+      __builtin_amdgcn_global_load_lds(base + (uint32_t)(row * 256 + (voff & 255)),
+                                       (__attribute__((address_space(3))) void*)(lds + (wave + 4 * it) * 1024),
+                                       16, 0, 0);
+    }
   }
 }
 
@@ -107,11 +125,15 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
   }
   if (j_end <= j_begin) return;
 
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int q4 = lane >> 4;
   const int c16 = lane & 15;
   const int64_t c0 = a.cu_c[s];
+  const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc + ((int64_t)g * a.c_rows + c0) * kHeadDim);
+  const int rmax = (int)(a.c_rows - 1 - c0);
+  const int lw = 4 * wave + q4;
+  const uint32_t voff = (uint32_t)(lw * 256 + ((c16 ^ (lw & 7)) << 4));
 
   int tpos[kTPW], nv[kTPW], bt[kTPW];
   int64_t trow[kTPW];
@@ -150,6 +172,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
     }
   }
 
+  // Pass 1 row state, in the exp2 domain: offset m (scaled by c) and sum.
   float m[kTPW][4], ssum[kTPW][4], carry[kTPW];
 #pragma unroll
   for (int k = 0; k < kTPW; ++k) {
@@ -163,26 +186,51 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
   const int nv_first = n_visible(t_first, a.win_kernel, a.win_stride, nwin);
   const int ntiles = (j_end - j_begin + kWT - 1) / kWT;
 
-  // S^T chunk ct (16 windows x 16 heads) of the staged tile for all tokens of
-  // the wave: the four tokens' accumulators are independent MFMA chains.
-  auto chunk = [&](const uint8_t* cur, int ct, floatx4 (&acc)[kTPW]) {
-    bf16x8 b[4];
+  // B fragments of chunk ct (16 windows) and the S^T chunk (16 windows x 16
+  // heads) of every token of the wave: four independent MFMA chains.
+  auto frags = [&](const uint8_t* cur, int ct, bf16x8 (&b)[4]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) b[ks] = lds_window_frag(cur, 16 * ct + c16, 4 * ks + q4);
+  };
+  auto mm = [&](const bf16x8 (&b)[4], floatx4 (&acc)[kTPW]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
       for (int k = 0; k < kTPW; ++k)
         acc[k] = mfma16(qa[k][ks], b[ks], ks == 0 ? floatx4{0.f, 0.f, 0.f, 0.f} : acc[k]);
   };
+  auto chunk = [&](const uint8_t* cur, int ct, floatx4 (&acc)[kTPW]) {
+    bf16x8 b[4];
+    frags(cur, ct, b);
+    mm(b, acc);
+  };
+  // Walk over the chunks of a staged tile, software-pipelined: the MFMAs of
+  // chunk ct are issued (and the fragments of chunk ct + 1 read) before
+  // chunk ct - 1's scores are consumed, so one chunk's exponentials run
+  // while the matrix cores compute the next.
+  auto walk = [&](const uint8_t* cur, auto&& consume) {
+    bf16x8 b[2][4];
+    floatx4 acc[2][kTPW];
+    frags(cur, 0, b[0]);
+#pragma unroll
+    for (int ct = 0; ct < kCT; ++ct) {
+      sched_fence();
+      if (ct + 1 < kCT) frags(cur, ct + 1, b[(ct + 1) & 1]);
+      sched_fence();
+      mm(b[ct & 1], acc[ct & 1]);
+      if (ct > 0) consume(acc[(ct - 1) & 1], ct - 1);
+    }
+    sched_fence();
+    consume(acc[(kCT - 1) & 1], kCT - 1);
+  };
 
-  stage_windows(lds, a, g, c0, j_begin, wave, lane);
+  stage_windows(lds, kbase, j_begin, rmax, voff, lw, wave);
   for (int it = 0; it < ntiles; ++it) {
     const int jt = j_begin + it * kWT;
     const uint8_t* cur = lds + (it & 1) * (kWT * 256);
     __builtin_amdgcn_s_waitcnt(0);   // this wave's part of tile it has landed
     __syncthreads();                 // ... every wave's; the other buffer is free
-    if (it + 1 < ntiles) stage_windows(lds + ((it + 1) & 1) * (kWT * 256), a, g, c0, jt + kWT, wave, lane);
+    if (it + 1 < ntiles) stage_windows(lds + ((it + 1) & 1) * (kWT * 256), kbase, jt + kWT, rmax, voff, lw, wave);
 
     // Every window of the tile is visible to every token of the tile: no
     // per-score visibility test.
@@ -201,133 +249,149 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
             float mt = v;   // max over the 16 windows: lanes of this 16-lane row
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) mt = fmaxf(mt, __shfl_xor(mt, off));
-            m[k][r] = mt > -__builtin_inff() ? mt : 0.f;
+            m[k][r] = mt > -__builtin_inff() ? mt * a.c : 0.f;
           }
       }
       float st[kTPW][4];
-      // One straight-line body per case: full tiles carry no visibility select.
-      auto tile_sums = [&](auto full_c) {
-        constexpr bool kFull = decltype(full_c)::value;
+      if (full) {
+        walk(cur, [&](floatx4 (&acc)[kTPW], int ct) {
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          floatx4 acc[kTPW];
-          chunk(cur, ct, acc);
-#pragma unroll
-          for (int k = 0; k < kTPW; ++k) {
-            const bool ok = kFull || (jt + 16 * ct + c16 < nv[k]);
+          for (int k = 0; k < kTPW; ++k)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-              float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r] * a.c));
-              if (!kFull) e = ok ? e : 0.f;
+              const float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r]));
+              st[k][r] = ct == 0 ? e : st[k][r] + e;
+            }
+        });
+      } else {
+        walk(cur, [&](floatx4 (&acc)[kTPW], int ct) {
+#pragma unroll
+          for (int k = 0; k < kTPW; ++k) {
+            const bool ok = jt + 16 * ct + c16 < nv[k];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const float e = ok ? fast_exp2(fmaf(acc[k][r], a.c, -m[k][r])) : 0.f;
               st[k][r] = ct == 0 ? e : st[k][r] + e;
             }
           }
-        }
-      };
-      if (full) tile_sums(std::true_type{});
-      else tile_sums(std::false_type{});
-      // Rare paths, decided once per tile for the whole wave: a tile sum
-      // that overflowed (redo it with the exact tile max), and sums past 2^32
-      // (renormalise by a power of two).
-      bool bad = false, big = false;
+        });
+      }
+      // One test per tile for the whole wave: a new sum past 2^32, or a tile
+      // sum that overflowed (its new sum is then infinite).  Both are rare:
+      // an overflowed tile is redone with its exact max, a large sum is
+      // renormalised by a power of two.
+      float ns[kTPW][4];
+      float mx = 0.f;
 #pragma unroll
       for (int k = 0; k < kTPW; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          bad |= !(st[k][r] <= 3.0e38f);
-          big |= ssum[k][r] + st[k][r] > 4294967296.f;
+          ns[k][r] = ssum[k][r] + st[k][r];
+          mx = fmaxf(mx, ns[k][r]);
         }
-      if (__ballot(bad) != 0) {
-        float mt[kTPW][4];
+      if (__ballot(!(mx <= 4294967296.f)) != 0) {
+        bool bad = false;
 #pragma unroll
         for (int k = 0; k < kTPW; ++k)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) mt[k][r] = m[k][r];
+          for (int r = 0; r < 4; ++r) bad |= !(st[k][r] <= 3.0e38f);
+        if (__ballot(bad) != 0) {
+          float mt[kTPW][4];
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          floatx4 acc[kTPW];
-          chunk(cur, ct, acc);
+          for (int k = 0; k < kTPW; ++k)
 #pragma unroll
-          for (int k = 0; k < kTPW; ++k) {
-            const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+            for (int r = 0; r < 4; ++r) mt[k][r] = m[k][r];
+#pragma unroll 1
+          for (int ct = 0; ct < kCT; ++ct) {
+            floatx4 acc[kTPW];
+            chunk(cur, ct, acc);
 #pragma unroll
-            for (int r = 0; r < 4; ++r) mt[k][r] = fmaxf(mt[k][r], ok ? acc[k][r] : mt[k][r]);
+            for (int k = 0; k < kTPW; ++k) {
+              const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) mt[k][r] = fmaxf(mt[k][r], ok ? acc[k][r] * a.c : mt[k][r]);
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < kTPW; ++k)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              ns[k][r] = ssum[k][r] * fast_exp2(m[k][r] - mt[k][r]);
+              m[k][r] = mt[k][r];
+            }
+#pragma unroll 1
+          for (int ct = 0; ct < kCT; ++ct) {
+            floatx4 acc[kTPW];
+            chunk(cur, ct, acc);
+#pragma unroll
+            for (int k = 0; k < kTPW; ++k) {
+              const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r]));
+                ns[k][r] += ok ? e : 0.f;
+              }
+            }
           }
         }
 #pragma unroll
         for (int k = 0; k < kTPW; ++k)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            ssum[k][r] *= fast_exp2((m[k][r] - mt[k][r]) * a.c);
-            m[k][r] = mt[k][r];
-            st[k][r] = 0.f;
-          }
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          floatx4 acc[kTPW];
-          chunk(cur, ct, acc);
-#pragma unroll
-          for (int k = 0; k < kTPW; ++k) {
-            const bool ok = full || (jt + 16 * ct + c16 < nv[k]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const float e = fast_exp2(fmaf(acc[k][r], a.c, -m[k][r] * a.c));
-              st[k][r] += ok ? e : 0.f;
+            const float sn = ns[k][r];
+            if (sn > 4294967296.f) {
+              const int e2 = (int)__builtin_amdgcn_logf(sn);   // log2, truncated
+              ns[k][r] = ldexpf(sn, -e2);
+              m[k][r] += (float)e2;
             }
           }
-        }
       }
 #pragma unroll
       for (int k = 0; k < kTPW; ++k)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ssum[k][r] += st[k][r];
-      if (__ballot(big) != 0) {
-#pragma unroll
-        for (int k = 0; k < kTPW; ++k)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float sn = ssum[k][r];
-            if (sn > 4294967296.f) {
-              const int e2 = (int)__builtin_amdgcn_logf(sn);   // log2, truncated
-              ssum[k][r] = ldexpf(sn, -e2);
-              m[k][r] += (float)e2 / a.c;
-            }
-          }
-      }
+        for (int r = 0; r < 4; ++r) ssum[k][r] = ns[k][r];
     } else {
-      float sct[kTPW][4];
-      auto tile_probs = [&](auto full_c) {
-        constexpr bool kFull = decltype(full_c)::value;
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          floatx4 acc[kTPW];
-          chunk(cur, ct, acc);
+      float sct[kTPW][kCT];
+      if (full) {
+        walk(cur, [&](floatx4 (&acc)[kTPW], int ct) {
 #pragma unroll
           for (int k = 0; k < kTPW; ++k) {
             float sum = fast_exp2(fmaf(acc[k][0], a.c, -Lc[k][0]));
 #pragma unroll
             for (int r = 1; r < 4; ++r) sum += fast_exp2(fmaf(acc[k][r], a.c, -Lc[k][r]));
-            sct[k][ct] = (kFull || jt + 16 * ct + c16 < nv[k]) ? sum : 0.f;
+            sct[k][ct] = sum;
           }
-        }
-      };
-      if (full) tile_probs(std::true_type{});
-      else tile_probs(std::false_type{});
+        });
+      } else {
+        walk(cur, [&](floatx4 (&acc)[kTPW], int ct) {
 #pragma unroll
-      for (int k = 0; k < kTPW; ++k) {
-        // Reduce-scatter over the four 16-lane rows: afterwards lane l holds
-        // the group sum for window jt + l.
-        const float S = rs_x16(rs_x32(sct[k][0], sct[k][2]), rs_x32(sct[k][1], sct[k][3]));
-        // Quad max (windows 4b .. 4b+3) and the window before each quad
-        // (4b-1; lane 0 takes the previous tile's last window) via DPP.
-        const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));          // quad_perm 1,0,3,2
-        const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));       // quad_perm 2,3,0,1
-        const float prev = dpp_f32<0x138>(carry[k], S);          // wave_shr:1
-        carry[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 63));
-        if (need[k] && (lane & 3) == 0) {
-          const int b = (jt >> 2) + (lane >> 2);
-          if (b >= a.n_init && b <= bt[k] - a.n_local && b < a.bs_ld)
-            a.bs[((int64_t)g * a.rows_q + trow[k]) * a.bs_ld + b] = fmaxf(qm, prev);
+          for (int k = 0; k < kTPW; ++k) {
+            float sum = fast_exp2(fmaf(acc[k][0], a.c, -Lc[k][0]));
+#pragma unroll
+            for (int r = 1; r < 4; ++r) sum += fast_exp2(fmaf(acc[k][r], a.c, -Lc[k][r]));
+            sct[k][ct] = jt + 16 * ct + c16 < nv[k] ? sum : 0.f;
+          }
+        });
+      }
+#pragma unroll
+      for (int h = 0; h < kCT / 4; ++h) {
+        const int jh = jt + 64 * h;
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k) {
+          // Reduce-scatter over the four 16-lane rows: afterwards lane l
+          // holds the group sum for window jh + l.
+          const float S = rs_x16(rs_x32(sct[k][4 * h], sct[k][4 * h + 2]), rs_x32(sct[k][4 * h + 1], sct[k][4 * h + 3]));
+          // Quad max (windows 4b .. 4b+3) and the window before each quad
+          // (4b-1; lane 0 takes the previous 64 windows' last) via DPP.
+          const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));          // quad_perm 1,0,3,2
+          const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));       // quad_perm 2,3,0,1
+          const float prev = dpp_f32<0x138>(carry[k], S);          // wave_shr:1
+          carry[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 63));
+          if (need[k] && (lane & 3) == 0) {
+            const int b = (jh >> 2) + (lane >> 2);
+            if (b >= a.n_init && b <= bt[k] - a.n_local && b < a.bs_ld)
+              a.bs[((int64_t)g * a.rows_q + trow[k]) * a.bs_ld + b] = fmaxf(qm, prev);
+          }
         }
       }
     }
@@ -345,12 +409,13 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
           const float m2 = __shfl_xor(mm, off);
           const float s2 = __shfl_xor(ss, off);
           const float mn = fmaxf(mm, m2);
-          ss = ss * fast_exp2((mm - mn) * a.c) + s2 * fast_exp2((m2 - mn) * a.c);
+          ss = ss * fast_exp2(mm - mn) + s2 * fast_exp2(m2 - mn);
           mm = mn;
         }
         const int head = 4 * q4 + r;
         if (c16 == 0 && tval[k] && head < a.G && trow[k] < a.rows_q) {
-          const float L = ss > 0.f ? mm * a.scale + logf(ss) : -__builtin_inff();
+          // m is in log2 units: L = m ln 2 + ln(sum).
+          const float L = ss > 0.f ? mm * 0.6931471805599453f + logf(ss) : -__builtin_inff();
           a.lse[(int64_t)(g * a.G + head) * a.rows_q + trow[k]] = L;
         }
       }
