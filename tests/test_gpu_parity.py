@@ -312,11 +312,12 @@ def test_select_group16_ragged(lib, mode):
     say(f"  {stats}")
 
 
-@pytest.mark.parametrize("sel", [(0, 2, 9), (2, 0, 7), (1, 3, 0), (1, 2, 80), (0, 0, 64)])
+@pytest.mark.parametrize("sel", [(0, 2, 9), (2, 0, 7), (1, 3, 0), (1, 2, 80), (0, 0, 64), (40, 4, 20)])
 def test_select_budgets(lib, sel):
-    """Unusual budgets: no init, no local or no top-k blocks, and top-k
-    counts at and above 64 (the top-k kernel's lane-maximum bound applies
-    only up to 64), 8q/2kv, two ragged sequences, sampled rows."""
+    """Unusual budgets: no init, no local or no top-k blocks, top-k counts at
+    and above 64 (the top-k kernel's lane-maximum bound applies only up to
+    64), and 40 init blocks (pass 2 then starts at window 128, one scoring
+    tile in), 8q/2kv, two ragged sequences, sampled rows."""
     say(f"select budgets {sel}")
     lengths, h_q, h_kv = [12000, 7001], 8, 2
     p = R.Params(n_init=sel[0], n_local=sel[1], n_topk=sel[2], lse_mode="exact")
