@@ -173,10 +173,16 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
   }
 
   // Pass 1 row state, in the exp2 domain: offset m (scaled by c) and sum.
-  float m[kTPW][4], ssum[kTPW][4], carry[kTPW];
+  // Pass 2: the last window sum of the previous 64 windows (bit pattern),
+  // each token's block-score row and its last candidate block (-1: none).
+  float m[kTPW][4], ssum[kTPW][4];
+  int carry[kTPW], b_hi[kTPW];
+  float* bs_row[kTPW];
 #pragma unroll
   for (int k = 0; k < kTPW; ++k) {
-    carry[k] = 0.f;
+    carry[k] = 0;
+    b_hi[k] = need[k] ? (int)min((int64_t)(bt[k] - a.n_local), a.bs_ld - 1) : -1;
+    bs_row[k] = a.bs + ((int64_t)g * a.rows_q + min(trow[k], a.rows_q - 1)) * a.bs_ld;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       m[k][r] = 0.f;
@@ -376,22 +382,24 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
 #pragma unroll
       for (int h = 0; h < kCT / 4; ++h) {
         const int jh = jt + 64 * h;
+        // Block of this lane's quad, relative to the candidate range.
+        const int bq = (jh >> 2) + (lane >> 2);
 #pragma unroll
         for (int k = 0; k < kTPW; ++k) {
           // Reduce-scatter over the four 16-lane rows: afterwards lane l
           // holds the group sum for window jh + l.
           const float S = rs_x16(rs_x32(sct[k][4 * h], sct[k][4 * h + 2]), rs_x32(sct[k][4 * h + 1], sct[k][4 * h + 3]));
           // Quad max (windows 4b .. 4b+3) and the window before each quad
-          // (4b-1; lane 0 takes the previous 64 windows' last) via DPP.
-          const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));          // quad_perm 1,0,3,2
-          const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));       // quad_perm 2,3,0,1
-          const float prev = dpp_f32<0x138>(carry[k], S);          // wave_shr:1
-          carry[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 63));
-          if (need[k] && (lane & 3) == 0) {
-            const int b = (jh >> 2) + (lane >> 2);
-            if (b >= a.n_init && b <= bt[k] - a.n_local && b < a.bs_ld)
-              a.bs[((int64_t)g * a.rows_q + trow[k]) * a.bs_ld + b] = fmaxf(qm, prev);
-          }
+          // (4b-1; lane 0 takes the previous 64 windows' last) via DPP.  The
+          // sums are non-negative floats, ordered as their bit patterns, so
+          // the maxima are integer maxima.
+          const int si = __float_as_int(S);
+          const int q1 = max(si, __builtin_amdgcn_update_dpp(0, si, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+          const int qm = max(q1, __builtin_amdgcn_update_dpp(0, q1, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+          const int prev = __builtin_amdgcn_update_dpp(carry[k], si, 0x138, 0xF, 0xF, false);   // wave_shr:1
+          carry[k] = __builtin_amdgcn_readlane(si, 63);
+          if ((lane & 3) == 0 && bq >= a.n_init && bq <= b_hi[k])
+            bs_row[k][bq] = __int_as_float(max(qm, prev));
         }
       }
     }
