@@ -18,7 +18,8 @@
 // rows of a 16x16x32 MFMA tile and 16 compressed keys its columns, so each
 // lane ends up holding 4 heads of one window: the group sum is 3 in-lane adds
 // plus a reduce-scatter over the four 16-lane rows, after which lane l holds
-// S for window (tile start + l) and a quad max gives the block score.
+// S for window (start of its 64 windows + l) and a quad max gives the block
+// score.
 // Compressed-key tiles of 128 windows are staged in LDS (direct global->LDS
 // loads, double-buffered: the next tile lands while this one computes) and
 // shared by the 4 waves; each LDS fragment feeds 4 MFMAs (one per token).
@@ -33,8 +34,6 @@
 // wave).  Every exponent stays finite and the result is the same log-sum-exp,
 // with one FMA, one exp and one add per score on full tiles; the offset is
 // kept in log2 units (scaled by scale * log2 e), so L = m ln 2 + ln(sum).
-#include <type_traits>
-
 #include "kernels.hpp"
 
 namespace infllmv2 {
