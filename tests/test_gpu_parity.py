@@ -587,6 +587,33 @@ def test_split_select_short_queries(lib, mode):
                 assert ok, (s, i, g)
 
 
+def test_split_select_extreme_scores(lib):
+    """The split-K scoring kernels (4 and 2 queries at the end of the two
+    sequences of the extreme-score inputs) against the oracle's selection."""
+    say("split select extreme scores")
+    n, h_q, h_kv = 6000, 16, 1
+    klens, qlens = [n, n], [4, 2]
+    p = R.Params(n_init=1, n_local=4, n_topk=16, lse_mode="exact")
+    pr = p.with_(round_kc=True)
+    inp = _extreme_inputs(77, n, h_q)
+    kst = _starts(klens)
+    qrows = [kst[s] + klens[s] - qlens[s] + i for s in range(2) for i in range(qlens[s])]
+    qst = _starts(qlens)
+    plan = P.SparsePlan(qst, qlens, kst, klens, len(qrows), h_q, h_kv, _cfg(p))
+    plan.compress(to_dev(inp.k))
+    plan.select(to_dev(np.ascontiguousarray(inp.q[qrows])))
+    torch.cuda.synchronize()
+    idx = plan.block_idx.cpu().numpy()
+    for s in range(2):
+        KC1 = R.compress_keys(inp.k[kst[s]:kst[s] + klens[s]], 32, 16, True)
+        for i in range(qlens[s]):
+            t = klens[s] - qlens[s] + i
+            sel, diag = R.select_token(inp.q[kst[s] + t], t, KC1, None, h_q // h_kv, pr)
+            gl = [int(b) for b in idx[0, qst[s] + i] if b >= 0]
+            ok, _, _ = check_selection(gl, sel[0], diag["info"][0], t, pr)
+            assert ok, (s, i, gl, sel[0])
+
+
 @pytest.mark.parametrize("mode", ["exact", "approx"])
 def test_decode_steps(lib, mode):
     """Decode: incremental compression, selection for one new token per
