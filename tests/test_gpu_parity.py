@@ -587,6 +587,19 @@ def test_split_select_short_queries(lib, mode):
                 assert ok, (s, i, g)
 
 
+def test_end_to_end_extreme_scores(lib):
+    """Selection and attention on the extreme-score inputs: the attention
+    kernel's running max jumps by up to ~175 log2 units between blocks (its
+    rescale path), sampled rows from token 1800 on."""
+    say("end to end extreme scores")
+    n, h_q, h_kv = 6000, 16, 1
+    p = R.Params(n_init=1, n_local=4, n_topk=16, lse_mode="exact")
+    inp = _extreme_inputs(77, n, h_q)
+    pos = [sorted({t for t in sample_positions(n, 40, seed=50 + s) if t >= 1800} | {1800, 2047, 2048, 2111, 5999})
+           for s in range(2)]
+    _e2e(inp, [n, n], h_q, h_kv, p, pos)
+
+
 def test_split_select_extreme_scores(lib):
     """The split-K scoring kernels (4 and 2 queries at the end of the two
     sequences of the extreme-score inputs) against the oracle's selection."""
