@@ -1,7 +1,10 @@
-"""Shared test helpers: acceptance rules and small utilities (no method arithmetic)."""
+"""Shared test helpers: acceptance rules, small utilities and one seeded input
+builder (no method arithmetic)."""
 from __future__ import annotations
 
 import numpy as np
+
+from trainable_block_sparse_compress_amd import datagen as D
 
 REL_TIE = 1e-3       # selection tie band (relative), from the acceptance criteria
 ATT_MAX_ABS = 2e-2   # attention max-abs tolerance for bf16 I/O with fp32 accumulation
@@ -71,3 +74,43 @@ def sample_positions(n, count, seed=0, must=()):
     base |= {x for x in must if 0 <= x < n}
     extra = rng.choice(n, size=min(n, max(0, count - len(base))), replace=False)
     return sorted(base | set(int(x) for x in extra))
+
+
+def extreme_inputs(seed: int, n: int, h_q: int, flat: bool = False) -> D.PrefillInputs:
+    """Two sequences of n tokens, one KV head, whose keys from block 5 on
+    carry a large multiple alpha_b of the queries' common direction u, so
+    their scores sit far above those of the first 16 windows (blocks 0-4,
+    plain keys), which set pass 1's offset.  Sequence 0: alpha in [6, 9],
+    10 at block 32 when n > 2048 (scores up to ~165 log2 units above the
+    offset: tiles overflow and are redone with their exact max).  Sequence 1: alpha rising
+    from 1 to 4.5 over blocks 5-31, then in [3, 6] (at most ~100 above: sums
+    pass 2^32 and are renormalised, no tile overflows).  In both the top
+    candidates of every scored row stay within ~100 log2 units of its LSE,
+    so their fp32 scores do not underflow (rows from token 1800 on).
+
+    With flat=True every block from 5 on takes the same alpha (8 and 5): the
+    logits stay as large, but no key dominates a row (the gradients of a
+    row saturated on one key cancel to below the bf16 rounding of the
+    forward output that D = dO . O is taken from)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    d = 128
+    u = rng.choice([-1.0, 1.0], size=d)
+    tot = 2 * n
+    q = u[None, None, :] + 0.3 * rng.standard_normal((tot, h_q, d))
+    k = rng.standard_normal((tot, 1, d))
+    v = rng.standard_normal((tot, 1, d))
+    nblk = (n + 63) // 64
+    for s in range(2):
+        if flat:
+            alpha = np.full(nblk, 8.0 if s == 0 else 5.0)
+        elif s == 0:
+            alpha = rng.uniform(6.0, 9.0, size=nblk)
+            if nblk > 32:
+                alpha[32] = 10.0
+        else:
+            alpha = rng.uniform(3.0, 6.0, size=nblk)
+            alpha[5:32] = np.linspace(1.0, 4.5, 27)[:max(0, min(nblk, 32) - 5)]
+        alpha[:5] = 0.0
+        k[s * n:(s + 1) * n, 0, :] += np.repeat(alpha, 64)[:n, None] * u[None, :]
+    f = lambda x: D.f32_to_bf16_bits(x.astype(np.float32))
+    return D.PrefillInputs(q=f(q), k=f(k), v=f(v), cu_seqlens=np.array([0, n, tot], dtype=np.int32), seed=seed)

@@ -16,7 +16,7 @@ from trainable_block_sparse_compress_amd import binding as B
 from trainable_block_sparse_compress_amd import datagen as D
 from trainable_block_sparse_compress_amd import pipeline as P
 from tests.gpu_util import f64_to_bits, i32, say, to_bits, to_dev, to_f64
-from tests.helpers import (ATT_MAX_ABS, ATT_REL_RMS, attn_errors, check_selection,
+from tests.helpers import (ATT_MAX_ABS, ATT_REL_RMS, attn_errors, check_selection, extreme_inputs,
                            sample_positions)
 
 pytestmark = pytest.mark.gpu
@@ -312,38 +312,6 @@ def test_select_group16_ragged(lib, mode):
     say(f"  {stats}")
 
 
-def _extreme_inputs(seed: int, n: int, h_q: int) -> D.PrefillInputs:
-    """Two sequences of n tokens, one KV head, whose keys from block 5 on
-    carry a large multiple alpha_b of the queries' common direction u, so
-    their scores sit far above those of the first 16 windows (blocks 0-4,
-    plain keys), which set pass 1's offset.  Sequence 0: alpha in [6, 9],
-    10 at block 32 (scores up to ~165 log2 units above the offset: tiles
-    overflow and are redone with their exact max).  Sequence 1: alpha rising
-    from 1 to 4.5 over blocks 5-31, then in [3, 6] (at most ~100 above: sums
-    pass 2^32 and are renormalised, no tile overflows).  In both the top
-    candidates of every scored row stay within ~100 log2 units of its LSE,
-    so their fp32 scores do not underflow (rows from token 1800 on)."""
-    rng = np.random.Generator(np.random.PCG64(seed))
-    d = 128
-    u = rng.choice([-1.0, 1.0], size=d)
-    tot = 2 * n
-    q = u[None, None, :] + 0.3 * rng.standard_normal((tot, h_q, d))
-    k = rng.standard_normal((tot, 1, d))
-    v = rng.standard_normal((tot, 1, d))
-    nblk = (n + 63) // 64
-    for s in range(2):
-        if s == 0:
-            alpha = rng.uniform(6.0, 9.0, size=nblk)
-            alpha[32] = 10.0
-        else:
-            alpha = rng.uniform(3.0, 6.0, size=nblk)
-            alpha[5:32] = np.linspace(1.0, 4.5, 27)
-        alpha[:5] = 0.0
-        k[s * n:(s + 1) * n, 0, :] += np.repeat(alpha, 64)[:n, None] * u[None, :]
-    f = lambda x: D.f32_to_bf16_bits(x.astype(np.float32))
-    return D.PrefillInputs(q=f(q), k=f(k), v=f(v), cu_seqlens=np.array([0, n, tot], dtype=np.int32), seed=seed)
-
-
 def test_select_extreme_scores(lib):
     """Exact LSE through scores far above the first windows' (pass 1's
     overflowed-tile redo and its power-of-two renormalisation), G = 16,
@@ -352,7 +320,7 @@ def test_select_extreme_scores(lib):
     n, h_q, h_kv = 6000, 16, 1
     lengths = [n, n]
     p = R.Params(n_init=1, n_local=4, n_topk=16, lse_mode="exact")
-    inp = _extreme_inputs(77, n, h_q)
+    inp = extreme_inputs(77, n, h_q)
     _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
     # From token 1800 on every scored row has at least 20 candidate blocks past
     # block 4, so its n_topk-th score is far from fp32 underflow.
@@ -594,7 +562,7 @@ def test_end_to_end_extreme_scores(lib):
     say("end to end extreme scores")
     n, h_q, h_kv = 6000, 16, 1
     p = R.Params(n_init=1, n_local=4, n_topk=16, lse_mode="exact")
-    inp = _extreme_inputs(77, n, h_q)
+    inp = extreme_inputs(77, n, h_q)
     pos = [sorted({t for t in sample_positions(n, 40, seed=50 + s) if t >= 1800} | {1800, 2047, 2048, 2111, 5999})
            for s in range(2)]
     _e2e(inp, [n, n], h_q, h_kv, p, pos)
@@ -608,7 +576,7 @@ def test_split_select_extreme_scores(lib):
     klens, qlens = [n, n], [4, 2]
     p = R.Params(n_init=1, n_local=4, n_topk=16, lse_mode="exact")
     pr = p.with_(round_kc=True)
-    inp = _extreme_inputs(77, n, h_q)
+    inp = extreme_inputs(77, n, h_q)
     kst = _starts(klens)
     qrows = [kst[s] + klens[s] - qlens[s] + i for s in range(2) for i in range(qlens[s])]
     qst = _starts(qlens)
