@@ -439,13 +439,113 @@ def pin_grad_dense_torch():
             and _close(dV, v.grad.permute(1, 0, 2).numpy(), 1e-11))
 
 
+
+def _brute_select(Q, K, t, G, p: R.Params, scale):
+    """Selection of query t written out without the oracle's helpers:
+    compressed keys from a running sum, logits by einsum, the exact LSE as
+    scipy's softmax normaliser (or scipy's logsumexp over the coarse keys),
+    the group sum, the pool over windows enumerated by token overlap, and the
+    top-k by numpy's lexsort.  Returns (blocks per group, block scores or
+    None when no row score is needed)."""
+    n, h_kv, d = K.shape
+    csum = np.concatenate([np.zeros((1, h_kv, d)), np.cumsum(K, axis=0)])
+
+    def windows(l, s):
+        starts = [j for j in range(0, n) if j * s + l <= n]
+        return np.stack([(csum[j * s + l] - csum[j * s]) / l for j in starts], axis=1) if starts \
+            else np.zeros((h_kv, 0, d))
+
+    B = p.block_size
+    bt = t // B
+    init = set(range(min(p.n_init, bt + 1)))
+    local = set(range(max(0, bt - p.n_local + 1), bt + 1))
+    cands = [b for b in range(bt + 1) if p.n_init <= b <= bt - p.n_local]
+    if len(cands) <= p.n_topk:
+        return [sorted(init | local | set(cands))] * h_kv, None
+    KC1 = windows(p.c1_kernel, p.c1_stride)
+    vis1 = [j for j in range(KC1.shape[1]) if p.c1_stride * j + p.c1_kernel - 1 <= t]
+    z = scale * np.einsum("hd,hjd->hj", Q[t], KC1[np.arange(Q.shape[1]) // G][:, vis1])
+    if p.lse_mode == "exact":
+        P = softmax(z, axis=1)
+    else:
+        KC2 = windows(p.c2_kernel, p.c2_stride)
+        vis2 = [j for j in range(KC2.shape[1]) if p.c2_stride * j + p.c2_kernel - 1 <= t]
+        z2 = scale * np.einsum("hd,hjd->hj", Q[t], KC2[np.arange(Q.shape[1]) // G][:, vis2])
+        P = np.exp(z - logsumexp(z2, axis=1)[:, None])
+    S = P.reshape(h_kv, G, -1).sum(axis=1)
+    scores = np.zeros((h_kv, bt + 1))
+    out = []
+    for g in range(h_kv):
+        for b in range(bt + 1):
+            over = [i for i, j in enumerate(vis1)
+                    if p.c1_stride * j < B * (b + 1) and p.c1_stride * j + p.c1_kernel > B * b]
+            scores[g, b] = S[g, over].max() if over else 0.0
+        c = np.array(cands)
+        order = np.lexsort((c, -scores[g, c]))
+        out.append(sorted(init | local | set(c[order[:p.n_topk]].tolist())))
+    return out, scores
+
+
+def pin_select_token_brute():
+    """select_token (the whole selection of one query: LSE in the configured
+    mode, group-summed probabilities, max pool, top-k union) against the
+    brute-force pipeline above, in both LSE modes, for G = 2 and 4, on rows
+    before and after the first row that needs scores; the LSE is reported
+    exactly for the rows that need scores."""
+    for seed, (h_q, h_kv) in ((19, (4, 2)), (20, (8, 2))):
+        Q, K, _ = _tiny(seed, n=900, h_q=h_q, h_kv=h_kv, d=8)
+        G = h_q // h_kv
+        scale = 1 / math.sqrt(8)
+        for mode in ("exact", "approx"):
+            p = R.Params(n_init=1, n_local=2, n_topk=3, lse_mode=mode)
+            KC1 = R.compress_keys(K, 32, 16)
+            KC2 = R.compress_keys(K, 128, 64)
+            for t in (0, 63, 64, 383, 384, 447, 448, 500, 640, 767, 899):
+                idx, diag = R.select_token(Q[t], t, KC1, KC2, G, p)
+                want, scores = _brute_select(Q, K, t, G, p, scale)
+                if idx != want or diag["scored"] != (scores is not None):
+                    return False
+                if scores is None:
+                    if diag["L"] is not None:
+                        return False
+                    continue
+                bt = t // 64
+                cand = np.arange(p.n_init, bt - p.n_local + 1)
+                if not _close(diag["block_scores"][:, cand], scores[:, cand], 1e-11):
+                    return False
+                Lw = (R.lse_exact(Q[t], t, KC1, G, p) if mode == "exact"
+                      else R.lse_approx(Q[t], t, KC2, G, p))
+                nv = (len([j for j in range(KC1.shape[1]) if 16 * j + 31 <= t]) if mode == "exact"
+                      else len([j for j in range(KC2.shape[1]) if 64 * j + 127 <= t]))
+                kc = KC1 if mode == "exact" else KC2
+                Lb = [logsumexp(_brute_logits(Q[t], kc, G, scale, h, nv)) for h in range(h_q)]
+                if not (_close(diag["L"], Lb, 1e-11) and _close(Lw, Lb, 1e-11)):
+                    return False
+    return True
+
+
+def pin_bf16_decoding():
+    """as_f64 on bf16 bit patterns equals torch's bfloat16 -> float64
+    conversion for all 65536 patterns (signed zeros, subnormals, infinities
+    and NaNs included)."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(invalid="ignore"):          # signalling NaN patterns
+        got = R.as_f64(bits)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    if got.dtype != np.float64 or got.shape != want.shape:
+        return False
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    return bool(same.all() and np.array_equal(np.signbit(got), np.signbit(want))
+                and R.as_f64(np.array([0x3F80], dtype=np.uint16))[0] == 1.0)
+
+
 ALL_PINS = [pin_worked_example, pin_stage_parameters, pin_window_counts,
             pin_compress_by_convolution, pin_compress_constant, pin_compress_bf16_rounding,
             pin_lse_exact_scipy, pin_lse_approx_scipy, pin_group_sum_softmax,
             pin_constant_keys, pin_approx_bound, pin_pool_by_token_overlap,
             pin_topk_full_sort, pin_attention_sdpa, pin_attention_special_cases,
             pin_cost_identities, pin_grad_finite_differences, pin_grad_identities,
-            pin_grad_dense_torch]
+            pin_grad_dense_torch, pin_select_token_brute, pin_bf16_decoding]
 
 
 @pytest.mark.parametrize("pin", ALL_PINS, ids=lambda f: f.__name__)
@@ -558,6 +658,37 @@ def _wrong_attend_grad_dv_transposed(q, dout, K, V, keys_per_group, G, scale):  
     return dq, dk, dv
 
 
+
+def _wrong_as_f64(x):                                        # bits read as float16
+    a = np.asarray(x)
+    if a.dtype == np.uint16:
+        return a.view(np.float16).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def _select_token_variant(dispatch_swapped=False, gate=">"):
+    """select_token with its LSE dispatch swapped or its scoring gate changed."""
+    def fn(q, t, KC1, KC2, G, p):
+        h_kv = KC1.shape[0]
+        n_blocks = t // p.block_size + 1
+        lo, hi = R.candidate_range(t, p)
+        ncand = hi - lo + 1
+        need = {">": ncand > p.n_topk, ">=": ncand >= p.n_topk, "never": False}[gate]
+        if need:
+            exact = (p.lse_mode == "exact") != dispatch_swapped
+            L = R.lse_exact(q, t, KC1, G, p) if exact else R.lse_approx(q, t, KC2, G, p)
+            S = R.shared_scores(q, t, KC1, L, G, p)
+            bs = R.block_scores(S, n_blocks, p)
+        else:
+            L, bs = None, np.zeros((h_kv, n_blocks))
+        idx, infos = [], []
+        for g in range(h_kv):
+            blocks, info = R.select_from_scores(t, bs[g], p)
+            idx.append(blocks)
+            infos.append(info)
+        return idx, {"L": L, "block_scores": bs, "info": infos, "scored": need}
+    return fn
+
 _ORIG_ATTEND_GRAD = R._attend_grad
 
 
@@ -578,6 +709,10 @@ MUTATIONS = {
     "grad_without_delta_term": ("_attend_grad", _wrong_attend_grad_no_delta),
     "grad_dk_unscaled": ("_attend_grad", _wrong_attend_grad_unscaled_dk),
     "grad_dv_keys_reversed": ("_attend_grad", _wrong_attend_grad_dv_transposed),
+    "bf16_bits_read_as_fp16": ("as_f64", _wrong_as_f64),
+    "select_lse_dispatch_swapped": ("select_token", _select_token_variant(dispatch_swapped=True)),
+    "select_scores_gate_inclusive": ("select_token", _select_token_variant(gate=">=")),
+    "select_scores_never": ("select_token", _select_token_variant(gate="never")),
 }
 
 
