@@ -139,13 +139,14 @@ def compress_keys(K, kernel: int, stride: int, round_bf16: bool = False) -> np.n
 
 def compress_keys_incremental(K, prev: np.ndarray, kernel: int, stride: int,
                               round_bf16: bool = False) -> np.ndarray:
-    """Append the windows completed since ``prev`` was computed (decode)."""
-    K = as_f64(K)
+    """Append the windows completed since ``prev`` was computed (decode).
+    Only the key rows of the new windows are read."""
+    K = np.asarray(K)
     N = n_windows(K.shape[0], kernel, stride)
     have = prev.shape[1]
     new = np.empty((K.shape[1], N - have, K.shape[2]))
     for j in range(have, N):
-        new[:, j - have, :] = K[stride * j: stride * j + kernel].sum(axis=0) / kernel
+        new[:, j - have, :] = as_f64(K[stride * j: stride * j + kernel]).sum(axis=0) / kernel
     if round_bf16:
         new = round_to_bf16(new)
     return np.concatenate([prev, new], axis=1)
@@ -294,14 +295,14 @@ def _attend(q, t: int, K, V, keys_per_group, G: int, scale: float):
     h_q, d = q.shape
     o = np.zeros((h_q, d))
     lse = np.zeros(h_q)
-    for h in range(h_q):
-        g = h // G
-        u = keys_per_group[g]
-        z = scale * (K[u, g] @ q[h])
-        m = z.max()
-        w = np.exp(z - m)
-        o[h] = (w @ V[u, g]) / w.sum()
-        lse[h] = m + math.log(w.sum())
+    for g, u in enumerate(keys_per_group):
+        Ku, Vu = K[u, g], V[u, g]          # the group's keys and values, gathered once
+        for h in range(g * G, (g + 1) * G):
+            z = scale * (Ku @ q[h])
+            m = z.max()
+            w = np.exp(z - m)
+            o[h] = (w @ Vu) / w.sum()
+            lse[h] = m + math.log(w.sum())
     return o, lse
 
 

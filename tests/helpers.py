@@ -114,3 +114,27 @@ def extreme_inputs(seed: int, n: int, h_q: int, flat: bool = False) -> D.Prefill
         k[s * n:(s + 1) * n, 0, :] += np.repeat(alpha, 64)[:n, None] * u[None, :]
     f = lambda x: D.f32_to_bf16_bits(x.astype(np.float32))
     return D.PrefillInputs(q=f(q), k=f(k), v=f(v), cu_seqlens=np.array([0, n, tot], dtype=np.int32), seed=seed)
+
+
+BS_REL = 2e-3        # block scores: relative bar on entries above 1e-6 of the row max
+
+
+def check_block_scores(gpu_row, oracle_row, t, p, rel=BS_REL):
+    """Element-wise check of one (row, group) of block scores: the GPU writes
+    the candidate blocks n_init .. b_t - n_local only; each candidate whose
+    oracle score is above 1e-6 of the row's largest must match to ``rel``
+    relative, and every other candidate must lie below 2e-6 of that maximum.
+    Returns the number of entries compared."""
+    bt = t // p.block_size
+    c = np.arange(p.n_init, bt - p.n_local + 1)
+    if c.size == 0:
+        return 0
+    got = np.asarray(gpu_row, dtype=np.float64)[c]
+    want = np.asarray(oracle_row, dtype=np.float64)[c]
+    top = want.max()
+    big = want > 1e-6 * top
+    err = np.abs(got[big] - want[big]) / want[big]
+    assert np.all(np.isfinite(got)), ("non-finite block score", t)
+    assert err.max() <= rel, ("block score", t, float(err.max()), int(c[big][err.argmax()]))
+    assert np.all(got[~big] <= 2e-6 * top), ("small block score", t)
+    return int(big.sum())

@@ -224,3 +224,44 @@ def test_backward_validation(lib, kw, code):
     rc, _ = _bwd(lib, **kw)
     assert rc == code
     assert lib.infllmv2_last_error()
+
+
+def test_binding_rejects_mismatched_shapes():
+    """The Python binding checks every tensor's shape and dtype against the
+    sizes it passes to the C ABI before any pointer is taken (so this runs
+    on CPU tensors): a mismatch raises instead of reaching the kernels."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    bf, i32 = torch.bfloat16, torch.int32
+    q = torch.zeros((100, 4, 128), dtype=bf)
+    k = torch.zeros((100, 2, 128), dtype=bf)
+    cu = torch.zeros(2, dtype=i32)
+    idx = torch.zeros((2, 100, 8), dtype=i32)
+    bad = [
+        dict(out=torch.zeros((99, 4, 128), dtype=bf)),
+        dict(lse=torch.zeros((4, 99), dtype=torch.float32)),
+        dict(lse=torch.zeros((4, 100), dtype=torch.float16)),
+        dict(v=torch.zeros((100, 1, 128), dtype=bf)),
+        dict(v=torch.zeros((2, 128, 1, 64), dtype=bf), v_seq_stride=128),
+        dict(block_idx=torch.zeros((2, 99, 8), dtype=i32)),
+        dict(block_idx=torch.zeros((2, 100, 8), dtype=torch.int64)),
+        dict(cu_seqlens_q=torch.zeros(1, dtype=i32)),
+    ]
+    for kw in bad:
+        a = dict(q=q, k=k, v=k, cu_seqlens_q=cu, seqused_q=None, cu_seqlens_k=cu, seqused_k=None,
+                 batch=1, max_seqlen_q=100, max_seqlen_k=100, block_idx=idx, n_init=1, n_local=2,
+                 softmax_scale=0.1, out=torch.zeros_like(q), lse=None)
+        a.update(kw)
+        with pytest.raises(B.InfLLMv2Error):
+            B.sparse_attn(**a)
+    kc = torch.zeros((2, 5, 128), dtype=bf)
+    with pytest.raises(B.InfLLMv2Error):
+        B.select_blocks(q, kc, None, cu, None, cu, None, torch.zeros(1, dtype=i32), None, 1, 100, 100,
+                        1, 2, 5, 0.1, torch.zeros((2, 100, 7), dtype=i32), None)
+    with pytest.raises(B.InfLLMv2Error):
+        B.compress_k(k, cu, None, 1, 100, 32, 16, torch.zeros(1, dtype=i32),
+                     torch.zeros((2, 5, 64), dtype=bf))
+    with pytest.raises(B.InfLLMv2Error):
+        B.sparse_attn_bwd(q, k, k, q, torch.zeros((4, 100)), q, cu, None, cu, None, 1, 100, 100, idx,
+                          1, 2, 0.1, q, k, torch.zeros((100, 2, 64), dtype=bf), None)

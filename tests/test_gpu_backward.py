@@ -383,3 +383,103 @@ def test_backward_chunked_queries_and_empty_sequence(lib):
             mr, rr = grad_errors(got, ref)
             say(f"  seq {s} {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
             assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (s, name, mr, rr)
+
+
+def test_autograd_two_forwards_on_one_plan(lib):
+    """One SwitchPlan serves two forwards (different inputs, same lengths)
+    before either backward runs, as layers of equal lengths would: each
+    backward uses the block lists of its own forward.  Both gradients are
+    checked against the oracle on that forward's lists, and the two forwards'
+    lists differ (so reading the plan's current lists would be caught)."""
+    say("autograd: two forwards on one plan, then both backwards")
+    lengths, h_q, h_kv = [2500], 4, 2
+    G = h_q // h_kv
+    cfg = P.SparseConfig(n_init=1, n_local=4, n_topk=6, threshold=1024)
+    p = R.Params(n_init=1, n_local=4, n_topk=6)
+    plan = P.SwitchPlan(lengths, h_q, h_kv, cfg)
+    runs = []
+    for seed in (61, 62):
+        inp = D.make_prefill(seed, lengths, h_q, h_kv)
+        dO = D.make_grad(seed + 100, sum(lengths), h_q)
+        q, k, v = (to_dev(x).requires_grad_(True) for x in (inp.q, inp.k, inp.v))
+        out = P.attention_trainable(q, k, v, lengths, cfg, plan=plan)
+        runs.append((inp, dO, q, k, v, out, plan.sparse.block_idx.clone()))
+    assert not torch.equal(runs[0][6], runs[1][6])
+    for inp, dO, q, k, v, out, _ in reversed(runs):
+        (out.float() * to_dev(dO).float()).sum().backward()
+    torch.cuda.synchronize()
+    for inp, dO, q, k, v, out, idx_t in runs:
+        idx = idx_t.cpu().numpy()
+        sets = {t: [[int(b) for b in idx[g, t] if b >= 0] for g in range(h_kv)] for t in range(lengths[0])}
+        ref = R.attention_grad(inp.q, inp.k, inp.v, dO, G, p, sets)
+        for name, got, want in zip(("dq", "dk", "dv"), (q.grad, k.grad, v.grad), ref):
+            mr, rr = grad_errors(to_f64(got), want)
+            say(f"  {name}: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+            assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (name, mr, rr)
+
+
+def test_backward_128k_topk_blocks(lib):
+    """The 128K layer (32q/2kv, |I| = 1 + 32 + 63, lists from select_blocks,
+    the benchmark's launch configuration) with the upstream gradient zero
+    outside a set of rows R: dK and dV then sum over the rows of R only, so
+    the oracle can give them exactly.  R holds rows that attend each of 8
+    target blocks through their top-k entries (blocks far behind the row's
+    local window), plus spread rows.  Checked element-wise: dK / dV of the
+    target blocks and of every other key R touches, exact zeros elsewhere,
+    dq of the rows of R and exact zeros for the other rows."""
+    say("backward 128K, top-k-attended blocks")
+    n, h_q, h_kv = 131072, 32, 2
+    G = h_q // h_kv
+    p = R.Params()
+    inp = D.make_prefill(3, n, h_q, h_kv, n_needles=32)
+    cfg = P.SparseConfig()
+    plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    plan.compress(k)
+    plan.select(q)
+    torch.cuda.synchronize()
+    idx = plan.block_idx.cpu().numpy()
+    rng = np.random.Generator(np.random.PCG64(71))
+    bt = np.arange(n) // 64
+    targets, rows = [], set()
+    for b in rng.permutation(np.arange(200, 1900)):
+        if len(targets) == 8:
+            break
+        g = len(targets) % h_kv
+        hit = np.nonzero((idx[g] == b).any(axis=1) & (bt > b + p.n_local))[0]
+        if hit.size < 12:
+            continue
+        targets.append((int(b), g))
+        rows |= set(int(t) for t in rng.choice(hit, size=12, replace=False))
+    assert len(targets) == 8, targets
+    rows |= set(sample_positions(n, 16, seed=72))
+    rows = sorted(rows)
+    dO = np.zeros((n, h_q, 128), dtype=np.uint16)
+    dO[rows] = D.make_grad(73, len(rows), h_q)
+    dq, dk, dv = _run(q, k, v, [n], plan.block_idx, p, False, to_dev(dO))
+    Kf, Vf = R.as_f64(inp.k), R.as_f64(inp.v)
+    rq = np.zeros((len(rows), h_q, 128))
+    rk, rv = np.zeros((n, h_kv, 128)), np.zeros((n, h_kv, 128))
+    touched = np.zeros((n, h_kv), dtype=bool)
+    for i, t in enumerate(rows):
+        sets = [[int(x) for x in idx[g, t] if x >= 0] for g in range(h_kv)]
+        dqt, parts = R.attend_token_grad(inp.q[t], dO[t], t, Kf, Vf, sets, G, p)
+        rq[i] = dqt
+        for g, (u, gk, gv) in enumerate(parts):
+            rk[u, g] += gk
+            rv[u, g] += gv
+            touched[u, g] = True
+    say(f"  {len(rows)} rows, targets {targets}, {int(touched.sum())} keys touched")
+    mr, rr = grad_errors(dq[rows], rq)
+    say(f"  dq rows of R: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+    assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, ("dq", mr, rr)
+    others = np.setdiff1d(np.arange(n), rows)
+    assert np.all(dq[others] == 0.0)
+    for name, got, ref in (("dk", dk, rk), ("dv", dv, rv)):
+        for b, g in targets:
+            mr, rr = grad_errors(got[64 * b:64 * b + 64, g], ref[64 * b:64 * b + 64, g])
+            assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (name, b, g, mr, rr)
+        mr, rr = grad_errors(got[touched], ref[touched])
+        say(f"  {name} over touched keys: max-abs/max|ref| {mr:.2e}, rel RMS {rr:.2e}")
+        assert mr <= GRAD_MAX_REL and rr <= GRAD_REL_RMS, (name, mr, rr)
+        assert np.all(got[~touched] == 0.0), name

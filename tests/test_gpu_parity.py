@@ -16,8 +16,8 @@ from trainable_block_sparse_compress_amd import binding as B
 from trainable_block_sparse_compress_amd import datagen as D
 from trainable_block_sparse_compress_amd import pipeline as P
 from tests.gpu_util import f64_to_bits, i32, say, to_bits, to_dev, to_f64
-from tests.helpers import (ATT_MAX_ABS, ATT_REL_RMS, attn_errors, check_selection, extreme_inputs,
-                           sample_positions)
+from tests.helpers import (ATT_MAX_ABS, ATT_REL_RMS, attn_errors, check_block_scores, check_selection,
+                           extreme_inputs, sample_positions)
 
 pytestmark = pytest.mark.gpu
 
@@ -250,6 +250,18 @@ def test_split_path_short_queries(lib, h_q, h_kv):
 # selection
 # ----------------------------------------------------------------------------
 
+def _block_scores(plan, h_q, rows_q, rows):
+    """Block scores of the given global query rows from the select
+    workspace: fp32 [h_kv, rows_q, bs_ld] after the fp32 LSE [h_q, rows_q]
+    (256-byte aligned), bs_ld = ceil(max_k / 64) rounded up to 4."""
+    lse_bytes = (h_q * rows_q * 4 + 255) // 256 * 256
+    bs_ld = ((plan.max_k + 63) // 64 + 3) // 4 * 4
+    n = plan.h_kv * rows_q * bs_ld
+    bs = plan.ws_select[lse_bytes:lse_bytes + 4 * n].view(torch.float32).view(plan.h_kv, rows_q, bs_ld)
+    sel = torch.as_tensor(np.asarray(rows, dtype=np.int64), device=bs.device)
+    return dict(zip([int(r) for r in rows], bs.index_select(1, sel).permute(1, 0, 2).cpu().numpy()))
+
+
 def _run_select(inp, lengths, h_q, h_kv, p: R.Params):
     st = _starts(lengths)
     plan = P.SparsePlan(st, lengths, st, lengths, sum(lengths), h_q, h_kv, _cfg(p))
@@ -261,11 +273,17 @@ def _run_select(inp, lengths, h_q, h_kv, p: R.Params):
     return plan, plan.block_idx.cpu().numpy(), lse.cpu().numpy()
 
 
-def _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, positions_by_seq):
+def _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, positions_by_seq, plan=None):
+    """Selection (and the LSE of scored rows) of the given positions against
+    the oracle; with ``plan``, also the block scores element-wise."""
     pr = p.with_(round_kc=True)
     st = _starts(lengths)
     G = h_q // h_kv
-    stats = {"rows": 0, "scored": 0, "exempt": 0, "band": 0}
+    stats = {"rows": 0, "scored": 0, "exempt": 0, "band": 0, "scores": 0}
+    bsd = {}
+    if plan is not None:
+        bsd = _block_scores(plan, h_q, sum(lengths),
+                            [st[s] + t for s in range(len(lengths)) for t in positions_by_seq[s]])
     for s, n in enumerate(lengths):
         Ks = inp.k[st[s]:st[s] + n]
         KC1 = R.compress_keys(Ks, 32, 16, True)
@@ -283,6 +301,8 @@ def _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, positions_by_seq):
                 stats["exempt"] += int(exempt)
                 stats["band"] += band
                 stats["rows"] += 1
+                if bsd and diag["scored"]:
+                    stats["scores"] += check_block_scores(bsd[st[s] + t][g], diag["block_scores"][g], t, pr)
     return stats
 
 
@@ -293,8 +313,8 @@ def test_select_tiny_all_rows(lib, mode):
     lengths, h_q, h_kv = [4096], 2, 1
     p = R.Params(n_init=1, n_local=4, n_topk=11, lse_mode=mode)
     inp = D.make_prefill(1, lengths, h_q, h_kv)
-    _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
-    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, [range(4096)])
+    plan, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
+    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, [range(4096)], plan)
     say(f"  {stats}")
 
 
@@ -306,9 +326,9 @@ def test_select_group16_ragged(lib, mode):
     lengths, h_q, h_kv = [9001, 6300], 32, 2
     p = R.Params(lse_mode=mode)
     inp = D.make_prefill(6, lengths, h_q, h_kv, n_needles=4)
-    _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
+    plan, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
     pos = [sample_positions(n, 40, seed=s, must=(6143, 6144, 6145, 6207, 6208)) for s, n in enumerate(lengths)]
-    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos)
+    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos, plan)
     say(f"  {stats}")
 
 
@@ -321,12 +341,12 @@ def test_select_extreme_scores(lib):
     lengths = [n, n]
     p = R.Params(n_init=1, n_local=4, n_topk=16, lse_mode="exact")
     inp = extreme_inputs(77, n, h_q)
-    _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
+    plan, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
     # From token 1800 on every scored row has at least 20 candidate blocks past
     # block 4, so its n_topk-th score is far from fp32 underflow.
     pos = [sorted(set(range(1800, 2720, 11)) | {t for t in sample_positions(n, 30, seed=30 + s) if t >= 1800})
            for s in range(2)]
-    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos)
+    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos, plan)
     assert stats["scored"] > 100
     assert float(lse[:, 2500].max()) > 100.0     # the jump reached the LSE of a scored row
     say(f"  {stats}")
@@ -342,9 +362,9 @@ def test_select_budgets(lib, sel):
     lengths, h_q, h_kv = [12000, 7001], 8, 2
     p = R.Params(n_init=sel[0], n_local=sel[1], n_topk=sel[2], lse_mode="exact")
     inp = D.make_prefill(8, lengths, h_q, h_kv, n_needles=3)
-    _, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
+    plan, idx, lse = _run_select(inp, lengths, h_q, h_kv, p)
     pos = [sample_positions(n, 40, seed=10 + s) for s, n in enumerate(lengths)]
-    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos)
+    stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse, pos, plan)
     say(f"  {stats}")
 
 
@@ -363,7 +383,7 @@ def _e2e(inp, lengths, h_q, h_kv, p: R.Params, positions_by_seq, check_sel=True)
     idx = plan.block_idx.cpu().numpy()
     lse_s = plan.ws_select[:h_q * sum(lengths) * 4].view(torch.float32).view(h_q, sum(lengths)).cpu().numpy()
     if check_sel:
-        stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse_s, positions_by_seq)
+        stats = _check_rows(inp, lengths, h_q, h_kv, p, idx, lse_s, positions_by_seq, plan)
         say(f"  selection {stats}")
     of, lf = to_f64(out), lse_o.cpu().numpy()
     G = h_q // h_kv
@@ -458,18 +478,26 @@ def test_32k_sampled(lib, mode):
     n = 32768
     p = R.Params(lse_mode=mode)
     inp = D.make_prefill(2, n, 32, 2, n_needles=8)
-    pos = sample_positions(n, 24, seed=2, must=(6143, 6144, 20000 - 1))
+    pos = sample_positions(n, 256, seed=2, must=(6143, 6144, 20000 - 1))
     _e2e(inp, [n], 32, 2, p, [pos])
 
 
 @pytest.mark.parametrize("mode", ["exact", "approx"])
 def test_128k_sampled(lib, mode):
-    """n = 131072 (2048 blocks) with 32 needle blocks; sampled rows."""
+    """n = 131072 (2048 blocks) with 32 needle blocks, the benchmark's
+    prefill: 544 rows per mode, namely all 16 rows of 24 query tiles spread
+    over the sequence (every row slot of the scoring, top-k and attention
+    tiles) and 160 spread rows, both KV groups of each; selection, LSE, block
+    scores and attention against the oracle."""
     say(f"128K end-to-end {mode}")
     n = 131072
     p = R.Params(lse_mode=mode)
     inp = D.make_prefill(3, n, 32, 2, n_needles=32)
-    pos = sample_positions(n, 10, seed=3, must=(6144, 131071))
+    rng = np.random.Generator(np.random.PCG64(3))
+    tiles = rng.choice(np.arange(6144 // 16, n // 16), size=24, replace=False)
+    tile_rows = {int(16 * t + r) for t in tiles for r in range(16)}
+    pos = sorted(tile_rows | set(sample_positions(n, 160, seed=3, must=(6144, 131071))))
+    assert len(pos) >= 512
     _e2e(inp, [n], 32, 2, p, [pos])
 
 

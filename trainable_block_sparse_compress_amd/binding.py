@@ -108,6 +108,31 @@ def _bf16(t, name):
     return _ptr(t)
 
 
+def _shape(t, name, shape, dtype=None):
+    """A tensor argument must have exactly ``shape`` (and ``dtype``)."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise InfLLMv2Error(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise InfLLMv2Error(f"{name} must be {dtype}")
+
+
+def _meta(t, name, count):
+    """Per-sequence metadata: int32 with at least ``count`` entries."""
+    if t is None:
+        return
+    if t.dtype != torch.int32 or t.dim() != 1 or t.numel() < count:
+        raise InfLLMv2Error(f"{name} must be a 1-D int32 tensor of at least {count} entries")
+
+
+def _seq_meta(batch, cu_q, used_q, cu_k, used_k):
+    _meta(cu_q, "cu_seqlens_q", batch + (0 if used_q is not None else 1))
+    _meta(used_q, "seqused_q", batch)
+    _meta(cu_k, "cu_seqlens_k", batch + (0 if used_k is not None else 1))
+    _meta(used_k, "seqused_k", batch)
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
@@ -124,6 +149,11 @@ def compress_k(k, cu_seqlens_k, seqused_k, batch, max_seqlen_k, kernel_size, str
                k_cmp, cmp_begin=None, max_new=0):
     """k [rows_k, h_kv, d] bf16 -> k_cmp [h_kv, c_rows, d] bf16 (in place)."""
     rows_k, h_kv, d = k.shape
+    _shape(k_cmp, "k_cmp", (h_kv, k_cmp.shape[1], d))
+    _meta(cu_seqlens_k, "cu_seqlens_k", batch + (0 if seqused_k is not None else 1))
+    _meta(seqused_k, "seqused_k", batch)
+    _meta(cu_cmp, "cu_cmp", batch)
+    _meta(cmp_begin, "cmp_begin", batch)
     _check(load().infllmv2_compress_k(
         _bf16(k, "k"), _i32(cu_seqlens_k, "cu_seqlens_k"), _i32(seqused_k, "seqused_k"), batch,
         max_seqlen_k, rows_k, h_kv, d, kernel_size, stride, _i32(cu_cmp, "cu_cmp"),
@@ -147,6 +177,12 @@ def select_blocks(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_
     rows_q, h_q, d = q.shape
     h_kv, c1_rows, _ = k_c1.shape
     c2_rows = k_c2.shape[1] if k_c2 is not None else 0
+    _shape(k_c1, "k_c1", (h_kv, c1_rows, d))
+    _shape(k_c2, "k_c2", (h_kv, c2_rows, d))
+    _shape(block_idx, "block_idx", (h_kv, rows_q, n_init + n_local + n_topk), torch.int32)
+    _seq_meta(batch, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k)
+    _meta(cu_c1, "cu_c1", batch)
+    _meta(cu_c2, "cu_c2", batch if k_c2 is not None else 0)
     ws, ws_bytes = _ws(workspace)
     _check(load().infllmv2_select_blocks(
         _bf16(q, "q"), _bf16(k_c1, "k_c1"), _bf16(k_c2, "k_c2"), _i32(cu_seqlens_q, "cu_seqlens_q"),
@@ -175,12 +211,27 @@ def attn_workspace(h_q, h_kv, batch, max_seqlen_q, max_seqlen_k, rows_q, v_seq_s
     return size.value
 
 
+def _attn_shapes(q, k, v, out, lse, v_seq_stride, batch):
+    rows_q, h_q, d = q.shape
+    rows_k, h_kv, _ = k.shape
+    _shape(k, "k", (rows_k, h_kv, d))
+    _shape(out, "out", (rows_q, h_q, d))
+    _shape(lse, "lse", (h_q, rows_q), torch.float32)
+    if v_seq_stride == 0:
+        _shape(v, "v", (rows_k, h_kv, d))
+    else:
+        _shape(v, "v (transposed)", (h_kv, d, batch, v_seq_stride))
+
+
 def sparse_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch, max_seqlen_q,
                 max_seqlen_k, block_idx, n_init, n_local, softmax_scale, out, lse=None,
                 workspace=None, v_seq_stride=0, block_size=64):
     rows_q, h_q, d = q.shape
     rows_k, h_kv, _ = k.shape
     n_sel = block_idx.shape[-1]
+    _attn_shapes(q, k, v, out, lse, v_seq_stride, batch)
+    _shape(block_idx, "block_idx", (h_kv, rows_q, n_sel), torch.int32)
+    _seq_meta(batch, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k)
     ws, ws_bytes = _ws(workspace)
     _check(load().infllmv2_sparse_attn(
         _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _i32(cu_seqlens_q, "cu_seqlens_q"),
@@ -194,6 +245,8 @@ def dense_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch,
                max_seqlen_k, softmax_scale, out, lse=None, workspace=None, v_seq_stride=0):
     rows_q, h_q, d = q.shape
     rows_k, h_kv, _ = k.shape
+    _attn_shapes(q, k, v, out, lse, v_seq_stride, batch)
+    _seq_meta(batch, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k)
     ws, ws_bytes = _ws(workspace)
     _check(load().infllmv2_dense_attn(
         _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _i32(cu_seqlens_q, "cu_seqlens_q"),
@@ -224,8 +277,15 @@ def sparse_attn_bwd(q, k, v, out, lse, dout, cu_seqlens_q, seqused_q, cu_seqlens
     rows_q, h_q, d = q.shape
     rows_k, h_kv, _ = k.shape
     n_sel = block_idx.shape[-1] if block_idx is not None else 0
-    if lse is None or lse.dtype != torch.float32:
+    if lse is None:
         raise InfLLMv2Error("lse must be the forward's float32 [h_q, rows_q] LSE")
+    _shape(lse, "lse", (h_q, rows_q), torch.float32)
+    for name, t in (("out", out), ("dout", dout), ("dq", dq)):
+        _shape(t, name, (rows_q, h_q, d))
+    for name, t in (("v", v), ("dk", dk), ("dv", dv)):
+        _shape(t, name, (rows_k, h_kv, d))
+    _shape(block_idx, "block_idx", (h_kv, rows_q, n_sel), torch.int32)
+    _seq_meta(batch, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k)
     ws, ws_bytes = _ws(workspace)
     _check(load().infllmv2_sparse_attn_bwd(
         _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _bf16(out, "out"), _ptr(lse),

@@ -129,6 +129,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
   const int q4 = lane >> 4;
   const int c16 = lane & 15;
   const int64_t c0 = a.cu_c[s];
+  if (c0 < 0 || c0 >= a.c_rows) return;   // inconsistent metadata: nothing to read
   const uint8_t* kbase = reinterpret_cast<const uint8_t*>(a.kc + ((int64_t)g * a.c_rows + c0) * kHeadDim);
   const int rmax = (int)(a.c_rows - 1 - c0);
   const int lw = 4 * wave + q4;
@@ -500,7 +501,7 @@ __device__ __forceinline__ bool split_row(const ScoreArgs& a, int64_t row, Split
   const int nwin = rk.len >= a.win_kernel ? (rk.len - a.win_kernel) / a.win_stride + 1 : 0;
   r.nv = n_visible(r.t, a.win_kernel, a.win_stride, nwin);
   r.c0 = a.cu_c[r.s];
-  return true;
+  return r.c0 >= 0 && r.c0 < a.c_rows;   // inconsistent metadata: row skipped
 }
 
 // Key fragments of the 16-key chunk j0 .. j0+15 (B operand: lane c16 holds
@@ -509,6 +510,7 @@ __device__ __forceinline__ void chunk_keys(const ScoreArgs& a, int g, int64_t c0
                                            bf16x8 (&b)[4]) {
   int64_t rowc = c0 + j0 + c16;
   rowc = rowc < a.c_rows ? rowc : a.c_rows - 1;
+  rowc = rowc > 0 ? rowc : 0;
   const uint16_t* kp = a.kc + ((int64_t)g * a.c_rows + rowc) * kHeadDim + 8 * q4;
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) b[ks] = as_bf16x8(ldg16(kp + 32 * ks));

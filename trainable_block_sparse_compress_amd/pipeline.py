@@ -120,20 +120,22 @@ class SparsePlan:
         self.select(q)
         self.attend(q, k, v, out, lse)
 
-    def backward(self, q, k, v, out, lse, dout, dq, dk, dv):
-        """Gradients of the last ``run`` (its block lists held fixed) into
-        dq, dk, dv (rows of these sequences); the workspace is allocated on
-        first use and kept."""
+    def backward(self, q, k, v, out, lse, dout, dq, dk, dv, block_idx=None):
+        """Gradients into dq, dk, dv (rows of these sequences) with the block
+        lists held fixed: ``block_idx`` (the lists of the forward being
+        differentiated), by default the lists the last ``run`` left in the
+        plan.  The workspace is allocated on first use and kept."""
         if self.batch == 0:
             return
         c = self.cfg
+        idx = self.block_idx if block_idx is None else block_idx
         if getattr(self, "ws_bwd", None) is None:
             size = B.attn_bwd_workspace(q.shape[1], k.shape[1], self.batch, self.max_q, self.max_k,
                                         q.shape[0], k.shape[0], n_sel=c.n_sel, n_init=c.n_init,
                                         n_local=c.n_local)
             self.ws_bwd = torch.empty(max(1, size), dtype=torch.uint8, device=q.device)
         B.sparse_attn_bwd(q, k, v, out, lse, dout, self.cu_q, self.used_q, self.cu_k, self.used_k,
-                          self.batch, self.max_q, self.max_k, self.block_idx, c.n_init, c.n_local,
+                          self.batch, self.max_q, self.max_k, idx, c.n_init, c.n_local,
                           c.scale(self.d), dq, dk, dv, self.ws_bwd, block_size=c.block_size)
 
 
@@ -196,11 +198,13 @@ class SwitchPlan:
         self.dense.run(q, k, v, out, lse)
         self.sparse.run(q, k, v, out, lse)
 
-    def backward(self, q, k, v, out, lse, dout, dq, dk, dv):
-        """Gradients of the last ``run``; dense and sparse sequences write
-        disjoint rows of dq, dk, dv."""
+    def backward(self, q, k, v, out, lse, dout, dq, dk, dv, block_idx=None):
+        """Gradients of a forward of this plan (``block_idx``: the sparse
+        sequences' lists of that forward, by default those of the last
+        ``run``); dense and sparse sequences write disjoint rows of dq, dk,
+        dv."""
         self.dense.backward(q, k, v, out, lse, dout, dq, dk, dv)
-        self.sparse.backward(q, k, v, out, lse, dout, dq, dk, dv)
+        self.sparse.backward(q, k, v, out, lse, dout, dq, dk, dv, block_idx)
 
 
 def attention(q, k, v, seqlens, cfg: SparseConfig | None = None, lse=None):
@@ -215,22 +219,26 @@ def attention(q, k, v, seqlens, cfg: SparseConfig | None = None, lse=None):
 class _SwitchAttention(torch.autograd.Function):
     """Forward through the switch's kernels (the sparse sequences' block lists
     from select_blocks), backward through infllmv2_sparse_attn_bwd on the same
-    lists: the selection is held fixed, so no gradient reaches the scoring."""
+    lists: the selection is held fixed, so no gradient reaches the scoring.
+    The forward keeps its own copy of the lists, so a plan that serves
+    several forwards before their backwards (layers of equal lengths) gives
+    each backward the lists of its own forward."""
 
     @staticmethod
     def forward(ctx, q, k, v, plan):
         out = torch.empty_like(q)
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
         plan.run(q, k, v, out, lse)
-        ctx.save_for_backward(q, k, v, out, lse)
+        idx = plan.sparse.block_idx.clone() if plan.sparse.batch > 0 else None
+        ctx.save_for_backward(q, k, v, out, lse, idx)
         ctx.plan = plan
         return out
 
     @staticmethod
     def backward(ctx, dout):
-        q, k, v, out, lse = ctx.saved_tensors
+        q, k, v, out, lse, idx = ctx.saved_tensors
         dq, dk, dv = torch.zeros_like(q), torch.zeros_like(k), torch.zeros_like(v)
-        ctx.plan.backward(q, k, v, out, lse, dout.to(torch.bfloat16).contiguous(), dq, dk, dv)
+        ctx.plan.backward(q, k, v, out, lse, dout.to(torch.bfloat16).contiguous(), dq, dk, dv, idx)
         return dq, dk, dv, None
 
 
