@@ -81,39 +81,115 @@ def traffic_from_profile(kernel_src):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, n, h_q, h_kv, lse_mode, budget_s=15.0):
-    """The fp64 oracle on a bounded sample of the same workload: the full
-    stage-1 compression once, then whole rows (selection + attention) at
-    evenly spaced positions until the time budget is spent; the rate is
-    extrapolated to all n rows.  BLAS is limited to one thread."""
+def host_cores():
+    """Worker processes for the oracle baseline: the cores this process may
+    run on, capped by OMP_NUM_THREADS when it is set (the host's CPU share)."""
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# Oracle state shared with the forked baseline workers (copy-on-write).
+_ORACLE = {}
+
+
+def _oracle_rows(args):
+    """Worker: whole oracle rows (selection + attention) at the given
+    positions until the time budget is spent; returns the per-row times."""
+    positions, budget = args
     from threadpoolctl import threadpool_limits
 
     import oracle.reference as R
+    c = _ORACLE
+    times = []
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        for t in positions:
+            ts = time.perf_counter()
+            sel, _ = R.select_token(c["q"][t], t, c["KC1"], c["KC2"], c["G"], c["p"])
+            R.attend_token(c["q"][t], t, c["Kf"], c["Vf"], sel, c["G"], c["p"])
+            times.append(time.perf_counter() - ts)
+            if time.perf_counter() - t0 > budget:
+                break
+    return times
+
+
+def cpu_baseline(inp, n, h_q, h_kv, lse_mode, budget_s=15.0):
+    """The fp64 oracle on the host's cores, on a bounded sample of the same
+    workload: the stage-1 (and coarse) compression of all n tokens once, then
+    whole rows (selection + attention) at spread positions in worker
+    processes (one BLAS thread each) for about ``budget_s`` seconds of wall
+    time; the measured parallel row rate is extrapolated to all n rows.  Runs
+    before the GPU is touched (the workers are forked)."""
+    import multiprocessing as mp
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle.reference as R
+    cores = host_cores()
     p = R.Params(lse_mode=lse_mode, round_kc=True)
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
         KC1 = R.compress_keys(inp.k, 32, 16, True)
         KC2 = R.compress_keys(inp.k, 128, 64, True) if lse_mode == "approx" else None
-        Kf, Vf = R.as_f64(inp.k), R.as_f64(inp.v)
         t_pre = time.perf_counter() - t0
-        rows = 0
-        t1 = time.perf_counter()
-        positions = np.linspace(0, n - 1, 2048).astype(int)
-        order = np.random.Generator(np.random.PCG64(0)).permutation(positions)
-        for t in order:
-            t = int(t)
-            sel, _ = R.select_token(inp.q[t], t, KC1, KC2, h_q // h_kv, p)
-            R.attend_token(inp.q[t], t, Kf, Vf, sel, h_q // h_kv, p)
-            rows += 1
-            if time.perf_counter() - t1 > budget_s:
-                break
-        t_rows = time.perf_counter() - t1
-    per_row = t_rows / rows
-    value = n / (t_pre + n * per_row)
-    return {"value": value, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 oracle, 1 BLAS thread: stage-1 compression of all {n} tokens "
-                      f"({t_pre:.1f} s) + {rows} full rows (selection + attention) at spread "
-                      f"positions ({t_rows:.1f} s), extrapolated to {n} rows"}
+    _ORACLE.update(q=inp.q, KC1=KC1, KC2=KC2, Kf=R.as_f64(inp.k), Vf=R.as_f64(inp.v),
+                   G=h_q // h_kv, p=p)
+    positions = np.random.Generator(np.random.PCG64(0)).permutation(
+        np.linspace(0, n - 1, 64 * cores).astype(int))
+    jobs = [([int(t) for t in positions[w::cores]], budget_s) for w in range(cores)]
+    t1 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        per_worker = pool.map(_oracle_rows, jobs)
+    wall = time.perf_counter() - t1
+    _ORACLE.clear()
+    times = [x for w in per_worker for x in w]
+    rows = len(times)
+    rate = rows / wall                         # rows per second on `cores` processes
+    value = n / (t_pre + n / rate)
+    one_core = n / (t_pre + n * float(np.mean(times)))
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "cpu_model": cpu_model(), "value_1core": one_core,
+            "sample": f"fp64 oracle: stage-1{' and coarse' if KC2 is not None else ''} compression "
+                      f"of all {n} tokens ({t_pre:.1f} s, one process), then {rows} whole rows "
+                      f"(selection + attention) at spread positions on {cores} worker processes "
+                      f"(1 BLAS thread each) in {wall:.1f} s, extrapolated to {n} rows"}
+
+
+# L2 -> CU read bandwidth of MI355X: 16 L2 channels of 128 B/clk per XCD
+# (2048 B/clk), 8 XCDs, 2.4 GHz.  The gather roof of the attention kernel.
+PEAK_L2_GBS = 2048 * 8 * 2.4
+
+DECODE_BATCH, DECODE_CACHE, DECODE_STEPS = 16, 131072, 256
+
+
+def staged_bytes(idx):
+    """Bytes the tile attention kernel stages per launch: every 16-row query
+    tile stages each distinct block of its rows' block sets once (K and V,
+    64 x 128 bf16 each).  idx: int32 [h_kv, rows, n_sel], -1 padded."""
+    h_kv, rows, n_sel = idx.shape
+    nt = (rows + 15) // 16
+    total = 0
+    for g in range(h_kv):
+        x = np.full((nt * 16, n_sel), -1, dtype=np.int32)
+        x[:rows] = idx[g]
+        x = np.sort(x.reshape(nt, 16 * n_sel), axis=1)
+        distinct = (np.diff(x, axis=1) != 0).sum(axis=1) + 1 - (x[:, 0] < 0)
+        total += int(distinct.sum())
+    return total * 2 * 64 * 128 * 2
 
 
 def main():
@@ -125,12 +201,17 @@ def main():
     ap.add_argument("--lse", choices=["exact", "approx"], default="exact")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="prefill: skip the extra keys (approximate-LSE step, 256-step decode)")
+    ap.add_argument("--decode-steps", type=int, default=DECODE_STEPS,
+                    help="decode steps timed (the extra decode key and --workload decode)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="after the run, copy a buffer of this many MiB 3 times (a plain copy "
                          "kernel of known size, to calibrate HBM byte counters)")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="also time the dense causal kernel at the same length (context)")
-    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep", "backward", "layer"],
+    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep", "backward", "layer",
+                                           "layer_decode", "unfused"],
                     default="prefill",
                     help="prefill (default): one 128K sequence; decode: 16 sequences x 128K "
                          "cache, one token each per step; varlen: 65536 packed tokens of mixed "
@@ -138,7 +219,9 @@ def main():
                          "selection sizes |I| against the dense kernel at the same length; "
                          "backward: the gradients of the 128K sparse attention (selection "
                          "held fixed); layer: one attention layer of the 8B shape (hidden 4096) "
-                         "with its Q/K/V/O projections, sparse against dense")
+                         "with its Q/K/V/O projections, sparse against dense (prefill, time to "
+                         "first token); layer_decode: the same layer in decode (time per output "
+                         "token); unfused: block selection with and without the fused group sum")
     ap.add_argument("--no-graph", action="store_true",
                     help="decode: launch the step's kernels one by one instead of replaying "
                          "the captured HIP graph of the step")
@@ -160,22 +243,19 @@ def main():
         return bench_backward(args)
     if args.workload == "layer":
         return bench_layer(args)
+    if args.workload == "layer_decode":
+        return bench_layer_decode(args)
+    if args.workload == "unfused":
+        return bench_unfused(args)
+    return bench_prefill(args)
 
+
+def time_prefill(plan, q, k, vt, n, cfg, d, steps, warmup, out):
+    """Warmup, then `steps` timed steps of compress_k + select_blocks +
+    sparse_attn on the current stream: (ms per step, ms per stage)."""
     import torch
 
     from trainable_block_sparse_compress_amd import binding as B
-    from trainable_block_sparse_compress_amd import datagen as D
-    from trainable_block_sparse_compress_amd import pipeline as P
-
-    n, h_q, h_kv, d = args.seq, 32, 2, 128
-    print(f"[bench] generating inputs n={n}", file=sys.stderr, flush=True)
-    inp = D.make_prefill(3, n, h_q, h_kv, d, n_needles=32)
-    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
-    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
-    vt = v.permute(1, 2, 0).contiguous().view(h_kv, d, 1, n)   # caller-side layout, outside the timed region
-    out = torch.empty_like(q)
-    cfg = P.SparseConfig(lse_mode=args.lse)
-    plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -193,29 +273,62 @@ def main():
         if ev is not None:
             ev[3].record(stream)
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    print("[bench] timed steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0.record(stream)
-    for i in range(args.steps):
+    for i in range(steps):
         step(evs[i])
     t1.record(stream)
     torch.cuda.synchronize()
-    ms = t0.elapsed_time(t1) / args.steps
-    ms_compress = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    ms_select = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    ms_attn = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    ms = t0.elapsed_time(t1) / steps
+    stages = [float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs])) for j in range(3)]
+    return ms, stages
+
+
+def bench_prefill(args):
+    from trainable_block_sparse_compress_amd import datagen as D
+
+    n, h_q, h_kv, d = args.seq, 32, 2, 128
+    extras = not args.no_extras and n == 131072
+    print(f"[bench] generating inputs n={n}", file=sys.stderr, flush=True)
+    inp = D.make_prefill(3, n, h_q, h_kv, d, n_needles=32)
+    cpu = None
+    if not args.no_cpu:
+        # The oracle runs first, in forked workers, before the GPU is touched.
+        print(f"[bench] cpu baseline (oracle, {host_cores()} processes)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(inp, n, h_q, h_kv, args.lse, args.cpu_budget)
+    dec_inp = None
+    if extras:
+        print("[bench] decode inputs", file=sys.stderr, flush=True)
+        dec_inp = D.make_decode(4, DECODE_BATCH, DECODE_CACHE, 8 + args.decode_steps, h_q, h_kv, d,
+                                n_needles=32)
+
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    vt = v.permute(1, 2, 0).contiguous().view(h_kv, d, 1, n)   # caller-side layout, outside the timed region
+    out = torch.empty_like(q)
+    cfg = P.SparseConfig(lse_mode=args.lse)
+    plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
+    print("[bench] timed steps", file=sys.stderr, flush=True)
+    ms, (ms_compress, ms_select, ms_attn) = time_prefill(plan, q, k, vt, n, cfg, d, args.steps,
+                                                         args.warmup, out)
 
     w = algorithmic_work(n, h_q, h_kv, d)
     lse_flops = w["lse_exact_flops"] if args.lse == "exact" else w["lse_approx_flops"]
     mfma_flops = w["attn_flops"] + lse_flops + w["blocks_flops"]
     attn_tflops = w["attn_flops"] / (ms_attn * 1e-3) / 1e12
+    staged = staged_bytes(plan.block_idx.cpu().numpy())
+    gather_gbs = staged / (ms_attn * 1e-3) / 1e9
     kernel_src = os.path.join(ROOT, "trainable_block_sparse_compress_amd", "csrc", "attention.hip")
     traffic = traffic_from_profile(kernel_src) if (n == 131072 and args.lse == "exact") else None
     res = {
@@ -233,17 +346,46 @@ def main():
         "data": "synthetic: seeded i.i.d. N(0,1) bf16 Q/K/V with 32 planted needle blocks",
         "config": {"workload": f"sparse prefill, one layer, n={n}", "seq_len": n, "h_q": h_q,
                    "h_kv": h_kv, "head_dim": d, "block_size": 64, "n_init": 1, "n_local": 32,
-                   "n_topk": 63, "lse": args.lse},
+                   "n_topk": 63, "lse": args.lse,
+                   "v_layout": "transposed [h_kv, d, batch, n] (the attention kernel's; formed "
+                               "outside the timed region)"},
         "mfma_frac_of_peak": mfma_flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         "ms_compress_k": ms_compress,
         "ms_select_blocks": ms_select,
         "ms_sparse_attn": ms_attn,
         "roofline": {"bound": "mfma", "kernel": "attn_kernel (infllmv2_sparse_attn)",
                      "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic},
+                     "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": traffic,
+                     "gather": {"bytes_per_launch": staged, "achieved": gather_gbs,
+                                "peak": PEAK_L2_GBS, "unit": "GB/s", "frac": gather_gbs / PEAK_L2_GBS,
+                                "basis": "K and V of every distinct block of each 16-row query "
+                                         "tile, staged once per tile, over the kernel's time; "
+                                         "peak = L2->CU reads, 2048 B/clk per XCD x 8 x 2.4 GHz"}},
     }
+    if extras and args.lse == "exact":
+        print("[bench] approximate LSE", file=sys.stderr, flush=True)
+        cfg2 = P.SparseConfig(lse_mode="approx")
+        plan2 = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg2)
+        ms2, (c2, s2, a2) = time_prefill(plan2, q, k, vt, n, cfg2, d, args.steps, args.warmup, out)
+        f2 = w["attn_flops"] + w["lse_approx_flops"] + w["blocks_flops"]
+        res["approx_lse"] = {"value": n / (ms2 * 1e-3), "unit": "tokens/s", "ms_per_step": ms2,
+                             "steps": args.steps, "ms_compress_k": c2, "ms_select_blocks": s2,
+                             "ms_sparse_attn": a2,
+                             "mfma_frac_of_peak": f2 / (ms2 * 1e-3) / (PEAK_BF16_TFLOPS * 1e12)}
+        del plan2
+    if dec_inp is not None:
+        del plan
+        torch.cuda.empty_cache()
+        print(f"[bench] decode, {args.decode_steps} steps", file=sys.stderr, flush=True)
+        r = run_decode(dec_inp, DECODE_BATCH, DECODE_CACHE, args.decode_steps, 8, args.lse,
+                       graph=True)
+        res["decode"] = {"value": r["value"], "unit": "tokens/s", "ms_per_step": r["ms_per_step"],
+                         "steps": args.decode_steps, "workload": r["workload"],
+                         "launch": r["launch"], "hbm_frac": r["roofline"]["frac"],
+                         "hbm_gbs": r["roofline"]["achieved"]}
     if args.dense_steps > 0:
         print("[bench] dense kernel", file=sys.stderr, flush=True)
+        stream = torch.cuda.current_stream()
         dplan = P.DensePlan([0], [n], [0], [n], n, h_q, h_kv, cfg)
         dout = torch.empty_like(q)
         run_dense = lambda: B.dense_attn(q, k, vt, dplan.cu_q, dplan.used_q, dplan.cu_k,
@@ -271,56 +413,63 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         res["copy_calib_bytes"] = nb
-    if not args.no_cpu:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(inp, n, h_q, h_kv, args.lse, args.cpu_budget)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
-def bench_decode(args):
-    """Decode: batch 16, a 128K-token cache per sequence, one new token per
-    sequence per step (incremental compress_k, select_blocks, sparse_attn:
-    the split-K path), replayed as the captured HIP graph of the step
-    (--no-graph: the library calls one by one).  Timed per step with HIP
-    events around the replay (or the calls); the caller's cache append is
-    outside the timed region."""
+def decode_step_bytes(batch, len0, h_kv, n_sel, d=128):
+    """Algorithmic HBM bytes of one decode step: the stage-1 keys read once
+    (scoring), the selected K and V blocks of every sequence and KV group,
+    the block scores written and read, and the block lists."""
+    n1 = (len0 - 32) // 16 + 1
+    nblk = (len0 + 63) // 64
+    kc1_bytes = batch * h_kv * n1 * d * 2
+    kv_bytes = batch * h_kv * n_sel * 64 * d * 2 * 2
+    bs_bytes = 2 * batch * h_kv * nblk * 4 + batch * h_kv * n_sel * 4
+    return kc1_bytes + kv_bytes + bs_bytes
+
+
+def run_decode(inp, batch, len0, steps, warmup, lse_mode, graph=True):
+    """Decode over `warmup + steps` consecutive tokens per sequence of a
+    batch of `len0`-token caches (incremental compress_k, select_blocks,
+    sparse_attn: the split-K path), replayed as the captured HIP graph of
+    the step (graph=False: the library calls one by one).  Each step is
+    timed with HIP events around the replay (or the calls); the caller's
+    cache append and query placement are outside the timed region."""
     import torch
 
     from trainable_block_sparse_compress_amd import binding as B
-    from trainable_block_sparse_compress_amd import datagen as D
     from trainable_block_sparse_compress_amd import pipeline as P
 
-    batch, len0, h_q, h_kv, d = 16, args.seq, 32, 2, 128
-    nsteps = args.warmup + args.steps
-    print(f"[bench] decode inputs batch={batch} cache={len0}", file=sys.stderr, flush=True)
-    inp = D.make_decode(4, batch, len0, nsteps, h_q, h_kv, d, n_needles=32)
+    h_q, h_kv, d = inp.q_steps.shape[2], inp.k_steps.shape[2], inp.q_steps.shape[3]
+    nsteps = warmup + steps
     cap = (len0 + nsteps + 63) // 64 * 64
-    cfg = P.SparseConfig(lse_mode=args.lse)
+    cfg = P.SparseConfig(lse_mode=lse_mode)
     dec = P.DecodeState(batch, cap, h_q, h_kv, cfg)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
-    kc, vc = dev(inp.k_cache[:, :len0]), dev(inp.v_cache[:, :len0])
-    dec.fill([kc[s] for s in range(batch)], [vc[s] for s in range(batch)], [len0] * batch)
-    del kc, vc
+    for s in range(batch):
+        kc, vc = dev(inp.k_cache[s, :len0]), dev(inp.v_cache[s, :len0])
+        dec.fill_one(s, kc, vc)
+    dec.compress_all()
     qs, ks, vs = dev(inp.q_steps), dev(inp.k_steps), dev(inp.v_steps)
     out = torch.empty((batch, h_q, d), dtype=torch.bfloat16, device="cuda")
     stream = torch.cuda.current_stream()
     t_step, t_sel, t_attn = [], [], []
-    graph = None if args.no_graph else P.DecodeGraph(dec)
-    print(f"[bench] decode steps ({'eager' if graph is None else 'graph replay'})", file=sys.stderr,
-          flush=True)
+    g = P.DecodeGraph(dec) if graph else None
     for i in range(nsteps):
         old = dec.append(ks[i], vs[i])
         dec.step_prepare(old)
         q_new = qs[i].contiguous()
-        if graph is not None:
-            graph.q.copy_(q_new)          # the caller's input placement, outside the timed region
+        if g is not None:
+            g.q.copy_(q_new)          # the caller's input placement, outside the timed region
             torch.cuda.synchronize()
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
-            graph.graph.replay()
+            g.graph.replay()
             e1.record(stream)
             torch.cuda.synchronize()
-            if i >= args.warmup:
+            if i >= warmup:
                 t_step.append(e0.elapsed_time(e1))
             continue
         torch.cuda.synchronize()
@@ -342,31 +491,18 @@ def bench_decode(args):
                       dec.ws_attn, v_seq_stride=cap)
         ev[3].record(stream)
         torch.cuda.synchronize()
-        if i >= args.warmup:
+        if i >= warmup:
             t_step.append(ev[0].elapsed_time(ev[3]))
             t_sel.append(ev[1].elapsed_time(ev[2]))
             t_attn.append(ev[2].elapsed_time(ev[3]))
     ms = float(np.mean(t_step))
-    # Algorithmic HBM bytes per step: the stage-1 keys read once (scoring),
-    # the selected K and V blocks of every sequence and KV group, the block
-    # scores written and read, and the block lists.
-    n1 = (len0 - 32) // 16 + 1
-    nblk = (len0 + 63) // 64
-    kc1_bytes = batch * h_kv * n1 * d * 2
-    kv_bytes = batch * h_kv * cfg.n_sel * 64 * d * 2 * 2
-    bs_bytes = 2 * batch * h_kv * nblk * 4 + batch * h_kv * cfg.n_sel * 4
-    step_bytes = kc1_bytes + kv_bytes + bs_bytes
+    step_bytes = decode_step_bytes(batch, len0, h_kv, cfg.n_sel, d)
     gbs = step_bytes / (ms * 1e-3) / 1e9
-    res = {
-        "metric": "sparse-attn decode tokens/s (batch 16, 128K cache, 32q/2kv, d128, |I|=96)",
-        "value": batch / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16",
-        "data": "synthetic: seeded i.i.d. N(0,1) bf16 cache and step tokens, 32 needle blocks/seq",
-        "config": {"workload": f"decode, batch {batch}, cache {len0} per sequence, one token per "
-                               "sequence per step", "h_q": h_q, "h_kv": h_kv, "head_dim": d,
-                   "n_init": 1, "n_local": 32, "n_topk": 63, "lse": args.lse},
-        "launch": "eager" if graph is None else "HIP graph replay of the captured step",
+    return {
+        "value": batch / (ms * 1e-3), "ms_per_step": ms,
+        "workload": f"decode, batch {batch}, cache {len0} per sequence, {steps} consecutive "
+                    "tokens per sequence",
+        "launch": "eager" if g is None else "HIP graph replay of the captured step",
         "ms_select_blocks": float(np.mean(t_sel)) if t_sel else None,
         "ms_sparse_attn": float(np.mean(t_attn)) if t_attn else None,
         "roofline": {"bound": "hbm", "kernel": "whole decode step (compress_k + select_blocks + "
@@ -374,43 +510,79 @@ def bench_decode(args):
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                      "bytes_per_step": step_bytes, "traffic": None},
     }
+
+
+def bench_decode(args):
+    """Decode: batch 16, a 128K-token cache per sequence, one new token per
+    sequence per step, `--decode-steps` consecutive steps (see run_decode)."""
+    from trainable_block_sparse_compress_amd import datagen as D
+
+    batch, len0, h_q, h_kv, d = DECODE_BATCH, args.seq, 32, 2, 128
+    print(f"[bench] decode inputs batch={batch} cache={len0}", file=sys.stderr, flush=True)
+    inp = D.make_decode(4, batch, len0, 8 + args.decode_steps, h_q, h_kv, d, n_needles=32)
+    cpu = None
     if not args.no_cpu:
-        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline_decode(inp, batch, len0, h_q, h_kv, args.lse,
-                                                  args.cpu_budget)
+        print(f"[bench] cpu baseline (oracle, {host_cores()} processes)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline_decode(inp, batch, len0, h_q, h_kv, args.lse)
+    print(f"[bench] decode steps ({'eager' if args.no_graph else 'graph replay'})", file=sys.stderr,
+          flush=True)
+    r = run_decode(inp, batch, len0, args.decode_steps, 8, args.lse, graph=not args.no_graph)
+    res = {
+        "metric": "sparse-attn decode tokens/s (batch 16, 128K cache, 32q/2kv, d128, |I|=96)",
+        "value": r["value"], "unit": "tokens/s", "n_gpus": 1, "steps": args.decode_steps,
+        "warmup": 8, "ms_per_step": r["ms_per_step"], "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 cache and step tokens, 32 needle blocks/seq",
+        "config": {"workload": r["workload"], "h_q": h_q, "h_kv": h_kv, "head_dim": d,
+                   "n_init": 1, "n_local": 32, "n_topk": 63, "lse": args.lse},
+        "launch": r["launch"], "ms_select_blocks": r["ms_select_blocks"],
+        "ms_sparse_attn": r["ms_sparse_attn"], "roofline": r["roofline"],
+    }
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 
-def cpu_baseline_decode(inp, batch, len0, h_q, h_kv, lse_mode, budget_s=15.0):
-    """The fp64 oracle on the first decode step: stage-1 (and coarse) keys of
-    the caches, then selection + attention of each sequence's new token until
-    the budget is spent; extrapolated to one whole step of the batch.  The
-    compression of the whole cache is a one-time cost and not counted."""
+def _oracle_decode_row(s):
+    """Worker: selection + attention of sequence s's first new token."""
     from threadpoolctl import threadpool_limits
 
     import oracle.reference as R
-    p = R.Params(lse_mode=lse_mode, round_kc=True)
-    G = h_q // h_kv
-    done, t_rows = 0, 0.0
+    c = _ORACLE
     with threadpool_limits(limits=1):
-        for s in range(batch):
-            K = np.concatenate([inp.k_cache[s, :len0], inp.k_steps[0, s][None]], axis=0)
-            V = np.concatenate([inp.v_cache[s, :len0], inp.v_steps[0, s][None]], axis=0)
-            KC1 = R.compress_keys(K, 32, 16, True)
-            KC2 = R.compress_keys(K, 128, 64, True) if lse_mode == "approx" else None
-            Kf, Vf = R.as_f64(K), R.as_f64(V)
-            t0 = time.perf_counter()
-            sel, _ = R.select_token(inp.q_steps[0, s], len0, KC1, KC2, G, p)
-            R.attend_token(inp.q_steps[0, s], len0, Kf, Vf, sel, G, p)
-            t_rows += time.perf_counter() - t0
-            done += 1
-            if t_rows > budget_s:
-                break
-    per = t_rows / done
-    return {"value": 1.0 / per, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 oracle, 1 BLAS thread: selection + attention of the new token of "
-                      f"{done} of {batch} sequences at position {len0} ({t_rows:.1f} s); cache "
-                      f"compression not counted"}
+        t0 = time.perf_counter()
+        sel, _ = R.select_token(c["q"][s], c["t"], c["KC1"][s], c["KC2"][s], c["G"], c["p"])
+        R.attend_token(c["q"][s], c["t"], c["Kf"][s], c["Vf"][s], sel, c["G"], c["p"])
+        return time.perf_counter() - t0
+
+
+def cpu_baseline_decode(inp, batch, len0, h_q, h_kv, lse_mode):
+    """The fp64 oracle on the first decode step: the caches' compressed keys
+    are built first (a one-time cost, not counted), then the selection and
+    attention of every sequence's new token run in forked worker processes
+    (one BLAS thread each), timed as wall time for the whole batch."""
+    import multiprocessing as mp
+
+    import oracle.reference as R
+    cores = host_cores()
+    p = R.Params(lse_mode=lse_mode, round_kc=True)
+    K = [np.concatenate([inp.k_cache[s, :len0], inp.k_steps[0, s][None]]) for s in range(batch)]
+    V = [np.concatenate([inp.v_cache[s, :len0], inp.v_steps[0, s][None]]) for s in range(batch)]
+    _ORACLE.update(q=inp.q_steps[0], t=len0, G=h_q // h_kv, p=p,
+                   KC1=[R.compress_keys(x, 32, 16, True) for x in K],
+                   KC2=[R.compress_keys(x, 128, 64, True) if lse_mode == "approx" else None for x in K],
+                   Kf=[R.as_f64(x) for x in K], Vf=[R.as_f64(x) for x in V])
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(min(cores, batch)) as pool:
+        times = pool.map(_oracle_decode_row, range(batch))
+    wall = time.perf_counter() - t0
+    _ORACLE.clear()
+    return {"value": batch / wall, "unit": "tokens/s", "cores": min(cores, batch), "kind": "oracle",
+            "cpu_model": cpu_model(), "value_1core": batch / float(np.sum(times)),
+            "sample": f"fp64 oracle: selection + attention of the new token of all {batch} sequences "
+                      f"at position {len0} on {min(cores, batch)} worker processes (1 BLAS thread "
+                      f"each), {wall:.2f} s wall including the pool start; cache compression not "
+                      f"counted"}
 
 
 def bench_varlen(args):
@@ -718,3 +890,98 @@ def bench_layer(args):
 
 if __name__ == "__main__":
     main()
+
+
+def bench_layer_decode(args):
+    """One attention layer of the 8B GQA shape (hidden 4096, 32q/2kv, d128)
+    in decode, time per output token: batch 16, a 128K-token cache per
+    sequence; per step the Q/K/V projections of a seeded hidden state
+    (random weights, library GEMMs), the cache append of the new K and V
+    (one scatter each, positions from the device lengths), the sparse decode
+    step (incremental compress_k, select_blocks, sparse_attn) or our dense
+    kernel over the whole cache, then the output projection.  Every step is
+    timed with HIP events, launched eagerly."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import binding as B
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    batch, len0, hidden, h_q, h_kv, d = DECODE_BATCH, args.seq, 4096, 32, 2, 128
+    steps, warmup = args.decode_steps, 8
+    print(f"[bench] layer decode inputs batch={batch} cache={len0}", file=sys.stderr, flush=True)
+    inp = D.make_decode(4, batch, len0, 1, h_q, h_kv, d, n_needles=32)
+    cap = (len0 + warmup + steps + 63) // 64 * 64
+    cfg = P.SparseConfig(lse_mode=args.lse)
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    bf = torch.bfloat16
+    w = lambda i, o: (torch.randn((i, o), generator=gen, device="cuda", dtype=torch.float32)
+                      / math.sqrt(i)).to(bf)
+    wq, wk, wv, wo = w(hidden, h_q * d), w(hidden, h_kv * d), w(hidden, h_kv * d), w(h_q * d, hidden)
+    xs = torch.randn((warmup + steps, batch, hidden), generator=gen, device="cuda",
+                     dtype=torch.float32).to(bf)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    stream = torch.cuda.current_stream()
+    seq = torch.arange(batch, device="cuda")
+    out = torch.empty((batch, h_q, d), dtype=bf, device="cuda")
+
+    def run(sparse):
+        dec = P.DecodeState(batch, cap, h_q, h_kv, cfg)
+        for s in range(batch):
+            dec.fill_one(s, dev(inp.k_cache[s, :len0]), dev(inp.v_cache[s, :len0]))
+        dec.compress_all()
+        dcu = dec.cu_k
+        dws = None
+        if not sparse:
+            dws = torch.empty(max(1, B.attn_workspace(h_q, h_kv, batch, 1, cap, batch,
+                                                      v_seq_stride=cap)), dtype=torch.uint8,
+                              device="cuda")
+        times = []
+        for i in range(warmup + steps):
+            old = list(dec.lens)
+            dec.lens = [x + 1 for x in dec.lens]
+            pos = dec.used_k.clone()                 # device lengths before the append
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            x = xs[i]
+            q = (x @ wq).view(batch, h_q, d)
+            k_new = (x @ wk).view(batch, h_kv, d)
+            v_new = (x @ wv).view(batch, h_kv, d)
+            dec.k_cache.index_copy_(0, dcu.long() + pos.long(), k_new)
+            dec.vt_cache[:, :, seq, pos.long()] = v_new.permute(1, 2, 0)
+            dec.step_prepare(old)
+            if sparse:
+                dec.step(q, out, max(dec.lens))
+            else:
+                B.dense_attn(q, dec.k_cache, dec.vt_cache, dec.cu_q, dec.used_q, dec.cu_k,
+                             dec.used_k, batch, 1, max(dec.lens), cfg.scale(d), out, None, dws,
+                             v_seq_stride=cap)
+            y = out.view(batch, h_q * d) @ wo
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if i >= warmup:
+                times.append(e0.elapsed_time(e1))
+        del dec
+        torch.cuda.empty_cache()
+        return float(np.mean(times)), y
+
+    print("[bench] sparse layer decode", file=sys.stderr, flush=True)
+    ms_sparse, _ = run(True)
+    print("[bench] dense layer decode", file=sys.stderr, flush=True)
+    ms_dense, _ = run(False)
+    res = {
+        "metric": f"attention-layer decode tokens/s (time per output token; batch {batch}, "
+                  f"{len0}-token cache, hidden 4096, 32q/2kv, d128, |I|=96, with Q/K/V/O projections)",
+        "value": batch / (ms_sparse * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+        "warmup": warmup, "ms_per_step": ms_sparse, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) cache and hidden states, random projection weights",
+        "config": {"workload": f"one attention layer in decode (projections, cache append, sparse "
+                               f"step, output projection), batch {batch}, cache {len0}",
+                   "hidden": hidden, "h_q": h_q, "h_kv": h_kv, "head_dim": d, "lse": args.lse,
+                   "launch": "eager"},
+        "ms_dense_layer": ms_dense, "layer_speedup_vs_dense": ms_dense / ms_sparse,
+        "roofline": None,
+    }
+    print(json.dumps(res), flush=True)

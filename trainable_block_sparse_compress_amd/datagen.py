@@ -162,20 +162,33 @@ class DecodeInputs:
 
 def make_decode(seed: int, batch: int, len0: int, steps: int, h_q: int, h_kv: int,
                 d: int = 128, n_needles: int = 0, needle_scale: float = 0.5,
-                block_size: int = 64, needle_hi_margin: int = 33) -> DecodeInputs:
+                block_size: int = 64, needle_hi_margin: int = 33,
+                threads: int = 8) -> DecodeInputs:
     """Decode inputs: a KV cache of ``len0`` tokens per sequence plus ``steps``
     new (q, k, v) tokens per sequence.  Cache capacity is ``len0 + steps``.
 
-    Draw order: cache K, cache V, step Q, step K, step V, then per sequence the
-    needle ids and shift.  The needle direction is the unit mean of that
-    sequence's step queries over the group's heads.
+    Streams: ``SeedSequence(seed)`` is split into batch + 1 child streams.
+    Child s draws sequence s's cache K, then its cache V (so the sequences
+    can be drawn in parallel threads with the same result); the last child
+    draws the step Q, K, V, then the needle ids and shifts of each sequence.
+    The needle direction is the unit mean of that sequence's step queries over
+    the group's heads.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
+    from concurrent.futures import ThreadPoolExecutor
+
+    children = np.random.SeedSequence(seed).spawn(batch + 1)
     cap = len0 + steps
     k_cache = np.zeros((batch, cap, h_kv, d), dtype=np.uint16)
     v_cache = np.zeros((batch, cap, h_kv, d), dtype=np.uint16)
-    k_cache[:, :len0] = _draw_bf16(rng, (batch, len0, h_kv, d))
-    v_cache[:, :len0] = _draw_bf16(rng, (batch, len0, h_kv, d))
+
+    def draw_cache(s):
+        r = np.random.Generator(np.random.PCG64(children[s]))
+        k_cache[s, :len0] = _draw_bf16(r, (len0, h_kv, d))
+        v_cache[s, :len0] = _draw_bf16(r, (len0, h_kv, d))
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        list(ex.map(draw_cache, range(batch)))
+    rng = np.random.Generator(np.random.PCG64(children[batch]))
     q_steps = _draw_bf16(rng, (steps, batch, h_q, d))
     k_steps = _draw_bf16(rng, (steps, batch, h_kv, d))
     v_steps = _draw_bf16(rng, (steps, batch, h_kv, d))

@@ -294,10 +294,19 @@ class DecodeState:
     def fill(self, k_rows, v_rows, lens):
         """Load prefix K/V (lists of [len, h_kv, d] bf16 tensors) and compress."""
         for s, (kk, vv) in enumerate(zip(k_rows, v_rows)):
-            n = kk.shape[0]
-            self.k_cache[s * self.cap: s * self.cap + n] = kk
-            self.vt_cache[:, :, s, :n] = vv.permute(1, 2, 0)
-            self.lens[s] = n
+            self.fill_one(s, kk, vv)
+        self.compress_all()
+
+    def fill_one(self, s, k_rows, v_rows):
+        """Load sequence s's prefix K/V ([len, h_kv, d] bf16); compress_all
+        must follow once every sequence is loaded."""
+        n = k_rows.shape[0]
+        self.k_cache[s * self.cap: s * self.cap + n] = k_rows
+        self.vt_cache[:, :, s, :n] = v_rows.permute(1, 2, 0)
+        self.lens[s] = n
+
+    def compress_all(self):
+        """Compressed keys of the loaded prefixes."""
         self.used_k.copy_(torch.tensor(self.lens, dtype=torch.int32))
         c = self.cfg
         mx = max(self.lens)
