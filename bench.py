@@ -149,7 +149,7 @@ def cpu_baseline(inp, n, h_q, h_kv, lse_mode, budget_s=15.0):
     _ORACLE.update(q=inp.q, KC1=KC1, KC2=KC2, Kf=R.as_f64(inp.k), Vf=R.as_f64(inp.v),
                    G=h_q // h_kv, p=p)
     positions = np.random.Generator(np.random.PCG64(0)).permutation(
-        np.linspace(0, n - 1, 64 * cores).astype(int))
+        np.linspace(0, n - 1, 1024 * cores).astype(int))
     jobs = [([int(t) for t in positions[w::cores]], budget_s) for w in range(cores)]
     t1 = time.perf_counter()
     with mp.get_context("fork").Pool(cores) as pool:
@@ -888,9 +888,6 @@ def bench_layer(args):
     print(json.dumps(res), flush=True)
 
 
-if __name__ == "__main__":
-    main()
-
 
 def bench_layer_decode(args):
     """One attention layer of the 8B GQA shape (hidden 4096, 32q/2kv, d128)
@@ -985,3 +982,72 @@ def bench_layer_decode(args):
         "roofline": None,
     }
     print(json.dumps(res), flush=True)
+
+
+
+def bench_unfused(args):
+    """The fusion ablation of the selection: select_blocks (group sum fused
+    into the score kernel, block scores only reach HBM) against
+    select_blocks_unfused (every head's stage-1 probabilities written to HBM
+    and read back for the group sum and max pool), at n = 32768 and at
+    --seq, exact LSE, 32q/2kv, |I| = 96.  HIP-event times per call, the
+    S_C1 bytes the unfused path writes and reads, and the share of
+    (row, group) lists the two produce identically."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    h_q, h_kv, d = 32, 2, 128
+    stream = torch.cuda.current_stream()
+    rows = []
+    for n in sorted({32768, args.seq}):
+        print(f"[bench] unfused ablation n={n}", file=sys.stderr, flush=True)
+        inp = D.make_prefill(3 if n == 131072 else 2, n, h_q, h_kv, d,
+                             n_needles=32 if n == 131072 else 8)
+        dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+        q, k = dev(inp.q), dev(inp.k)
+        cfg = P.SparseConfig(lse_mode=args.lse)
+        res = {}
+        idx = {}
+        for unfused in (False, True):
+            plan = P.SparsePlan([0], [n], [0], [n], n, h_q, h_kv, cfg, unfused_select=unfused)
+            plan.compress(k)
+            for _ in range(args.warmup):
+                plan.select(q)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(args.steps):
+                plan.select(q)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[unfused] = e0.elapsed_time(e1) / args.steps
+            idx[unfused] = plan.block_idx.cpu().numpy()
+            del plan
+            torch.cuda.empty_cache()
+        t = np.arange(n)
+        bt = t // 64
+        scored = bt - 32 - 1 + 1 > 63
+        nv = np.clip((t - 31) // 16 + 1, 0, None)
+        sc1 = float(4 * h_q * nv[scored].sum())
+        rows.append({"n": n, "ms_select_fused": res[False], "ms_select_unfused": res[True],
+                     "unfused_over_fused": res[True] / res[False],
+                     "fused_time_cut": 1.0 - res[False] / res[True],
+                     "s_c1_bytes_written": sc1, "s_c1_bytes_read": sc1,
+                     "s_c1_gbs": 2 * sc1 / (res[True] * 1e-3) / 1e9,
+                     "identical_lists": float(np.mean(np.all(idx[False] == idx[True], axis=2)))})
+    head = rows[-1]
+    print(json.dumps({
+        "metric": "block selection ms per call, group sum fused into the score kernel vs unfused",
+        "value": head["ms_select_fused"], "unit": "ms", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": head["ms_select_fused"], "higher_is_better": False,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) bf16 Q/K with planted needle blocks",
+        "config": {"workload": f"select_blocks fused vs unfused, n in {[r['n'] for r in rows]}",
+                   "h_q": h_q, "h_kv": h_kv, "lse": args.lse}, "ablation": rows, "roofline": None,
+    }), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -153,6 +153,37 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
                            int32_t* block_idx, void* stream);
 
 /*
+ * infllmv2_select_blocks_unfused — the same selection without the fused
+ * group sum: the baseline of the fusion ablation (top168.com article,
+ * section 四 "高效实现的技术突破": written unfused, the stage-1 scores cost
+ * h_q * n^2 / s_C1 values of HBM traffic, and fusing the head-group sum
+ * into the score kernel divides that by G; the hegjx.blmgzj.com repost's
+ * ablation attributes part of the block-selection time to it).  Pass 2
+ * writes every head's probability exp(z[h, j] - L[h]) of every visible
+ * window to an fp32 buffer in HBM, in chunks of query rows; a second kernel
+ * reads them back, sums each group's heads and max-pools the sums into the
+ * same block scores; top-k is shared.  Same arguments, layouts, supported
+ * sizes and results (up to the order of the fp32 group sum) as
+ * infllmv2_select_blocks; the workspace adds the chunk buffer (at most 4 GiB:
+ * batch * chunk_rows * h_q * ceil(windows / 4) * 4 floats).  Always takes
+ * the tile kernels (no split-K path).  Not part of the fast path.
+ */
+int infllmv2_select_blocks_unfused(const void* q, const void* k_c1, const void* k_c2,
+                                   const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                                   const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                                   const int32_t* cu_c1, const int32_t* cu_c2,
+                                   int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                   int64_t rows_q, int64_t c1_rows, int64_t c2_rows,
+                                   int32_t h_q, int32_t h_kv, int32_t head_dim, int32_t block_size,
+                                   int32_t n_init, int32_t n_local, int32_t n_topk,
+                                   int32_t c1_kernel, int32_t c1_stride,
+                                   int32_t c2_kernel, int32_t c2_stride,
+                                   int32_t pool_kernel, int32_t pool_stride, int32_t pool_pad,
+                                   float softmax_scale,
+                                   void* workspace, size_t* workspace_bytes,
+                                   int32_t* block_idx, void* stream);
+
+/*
  * infllmv2_sparse_attn — block-sparse causal attention, the single output
  * branch (reading notes section "对齐计算图"; top168.com article section 七:
  * local blocks absorb the sliding window):

@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "InfLLMv2Error", "load", "library_path", "version", "compress_k", "select_blocks",
-    "select_blocks_workspace", "sparse_attn", "dense_attn", "attn_workspace",
+    "select_blocks_workspace", "select_blocks_unfused", "sparse_attn", "dense_attn", "attn_workspace",
     "sparse_attn_bwd", "attn_bwd_workspace",
 ]
 
@@ -35,6 +35,9 @@ _SIGS = {
     "infllmv2_select_blocks": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64,
                                _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
                                _I32, _I32, _I32, _I32, _F, _P, _SZP, _P, _P],
+    "infllmv2_select_blocks_unfused": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64,
+                                       _I64, _I64, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                       _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _SZP, _P, _P],
     "infllmv2_sparse_attn": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32, _I32,
                              _I32, _I32, _P, _I32, _I32, _I32, _F, _I64, _P, _P, _P, _SZP, _P],
     "infllmv2_dense_attn": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32, _I32,
@@ -161,9 +164,10 @@ def compress_k(k, cu_seqlens_k, seqused_k, batch, max_seqlen_k, kernel_size, str
 
 
 def select_blocks_workspace(rows_q, h_q, h_kv, max_seqlen_q, max_seqlen_k, n_init, n_local,
-                            n_topk, approx=False, batch=1) -> int:
+                            n_topk, approx=False, batch=1, unfused=False) -> int:
     size = ctypes.c_size_t(0)
-    _check(load().infllmv2_select_blocks(
+    fn = load().infllmv2_select_blocks_unfused if unfused else load().infllmv2_select_blocks
+    _check(fn(
         None, None, _P(1) if approx else None, None, None, None, None, None, None, batch,
         max_seqlen_q, max_seqlen_k, rows_q, 0, 0, h_q, h_kv, 128, 64, n_init, n_local, n_topk,
         32, 16, 128, 64, 5, 4, 1, 1.0, None, ctypes.byref(size), None, None))
@@ -172,7 +176,8 @@ def select_blocks_workspace(rows_q, h_q, h_kv, max_seqlen_q, max_seqlen_k, n_ini
 
 def select_blocks(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, cu_c1, cu_c2,
                   batch, max_seqlen_q, max_seqlen_k, n_init, n_local, n_topk, softmax_scale,
-                  block_idx, workspace, block_size=64, c1=(32, 16), c2=(128, 64), pool=(5, 4, 1)):
+                  block_idx, workspace, block_size=64, c1=(32, 16), c2=(128, 64), pool=(5, 4, 1),
+                  _entry="infllmv2_select_blocks"):
     """Writes block_idx [h_kv, rows_q, n_init + n_local + n_topk] int32."""
     rows_q, h_q, d = q.shape
     h_kv, c1_rows, _ = k_c1.shape
@@ -184,13 +189,20 @@ def select_blocks(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_
     _meta(cu_c1, "cu_c1", batch)
     _meta(cu_c2, "cu_c2", batch if k_c2 is not None else 0)
     ws, ws_bytes = _ws(workspace)
-    _check(load().infllmv2_select_blocks(
+    _check(getattr(load(), _entry)(
         _bf16(q, "q"), _bf16(k_c1, "k_c1"), _bf16(k_c2, "k_c2"), _i32(cu_seqlens_q, "cu_seqlens_q"),
         _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
         _i32(seqused_k, "seqused_k"), _i32(cu_c1, "cu_c1"), _i32(cu_c2, "cu_c2"), batch,
         max_seqlen_q, max_seqlen_k, rows_q, c1_rows, c2_rows, h_q, h_kv, d, block_size, n_init,
         n_local, n_topk, c1[0], c1[1], c2[0], c2[1], pool[0], pool[1], pool[2], softmax_scale,
         ws, ws_bytes, _i32(block_idx, "block_idx"), _stream()))
+
+
+def select_blocks_unfused(*args, **kw):
+    """select_blocks through infllmv2_select_blocks_unfused (the unfused
+    group-sum baseline; its workspace size comes from
+    select_blocks_workspace(..., unfused=True))."""
+    return select_blocks(*args, **kw, _entry="infllmv2_select_blocks_unfused")
 
 
 def attn_workspace(h_q, h_kv, batch, max_seqlen_q, max_seqlen_k, rows_q, v_seq_stride=0,

@@ -60,7 +60,13 @@ struct SelectLayout {
   int64_t bs_ld;
   int splits;                 // 0: tile kernels
   size_t lse_bytes, bs_bytes, part_bytes, total;
+  // Unfused baseline: per-head probabilities of chunk_rows query rows of
+  // every sequence, fp32 [batch, chunk_rows, h_q, sc1_ld].
+  int64_t sc1_ld = 0;
+  int chunk_rows = 0;
+  size_t sc1_bytes = 0;
 };
+constexpr size_t kUnfusedChunkBytes = size_t(4) << 30;   // bound of the chunk buffer
 // Workgroups the split scoring path aims for (measured best at batch 16:
 // 512 costs 7% more, 128 costs 20% more).
 constexpr int64_t kSelectTargetWgs = 256;
@@ -72,14 +78,22 @@ int select_splits(int64_t rows_q, int batch, int max_seqlen_q, int max_seqlen_k,
   return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, (int64_t)64}));
 }
 SelectLayout select_layout(int64_t rows_q, int batch, int max_seqlen_q, int h_q, int h_kv,
-                           int max_seqlen_k) {
+                           int max_seqlen_k, bool unfused = false) {
   SelectLayout L;
   L.bs_ld = round_up(std::max<int64_t>(1, ceil_div(max_seqlen_k, kBlock)), 4);
-  L.splits = select_splits(rows_q, batch, max_seqlen_q, max_seqlen_k, h_kv);
+  L.splits = unfused ? 0 : select_splits(rows_q, batch, max_seqlen_q, max_seqlen_k, h_kv);
   L.lse_bytes = align_up((size_t)h_q * (size_t)rows_q * sizeof(float));
   L.bs_bytes = align_up((size_t)h_kv * (size_t)rows_q * (size_t)L.bs_ld * sizeof(float));
   L.part_bytes = L.splits > 0 ? align_up((size_t)rows_q * h_kv * L.splits * 32 * sizeof(float)) : 0;
-  L.total = L.lse_bytes + L.bs_bytes + L.part_bytes;
+  if (unfused) {
+    const int64_t nwin = max_seqlen_k >= 32 ? (max_seqlen_k - 32) / 16 + 1 : 1;
+    L.sc1_ld = round_up(nwin, 4);
+    const size_t per_row = (size_t)std::max(1, batch) * h_q * (size_t)L.sc1_ld * sizeof(float);
+    const int64_t fit = std::max<int64_t>(16, (int64_t)(kUnfusedChunkBytes / per_row) / 16 * 16);
+    L.chunk_rows = (int)std::min<int64_t>(fit, round_up(std::max(1, max_seqlen_q), 16));
+    L.sc1_bytes = align_up(per_row * (size_t)L.chunk_rows);
+  }
+  L.total = L.lse_bytes + L.bs_bytes + L.part_bytes + L.sc1_bytes;
   return L;
 }
 
@@ -316,17 +330,21 @@ int infllmv2_compress_k(const void* k, const int32_t* cu_seqlens_k, const int32_
   return ok();
 }
 
-int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
-                           const int32_t* cu_seqlens_q, const int32_t* seqused_q,
-                           const int32_t* cu_seqlens_k, const int32_t* seqused_k,
-                           const int32_t* cu_c1, const int32_t* cu_c2, int32_t batch,
-                           int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t rows_q,
-                           int64_t c1_rows, int64_t c2_rows, int32_t h_q, int32_t h_kv,
-                           int32_t head_dim, int32_t block_size, int32_t n_init, int32_t n_local,
-                           int32_t n_topk, int32_t c1_kernel, int32_t c1_stride, int32_t c2_kernel,
-                           int32_t c2_stride, int32_t pool_kernel, int32_t pool_stride,
-                           int32_t pool_pad, float softmax_scale, void* workspace,
-                           size_t* workspace_bytes, int32_t* block_idx, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int select_common(const void* q, const void* k_c1, const void* k_c2,
+                  const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                  const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                  const int32_t* cu_c1, const int32_t* cu_c2, int32_t batch,
+                  int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t rows_q,
+                  int64_t c1_rows, int64_t c2_rows, int32_t h_q, int32_t h_kv,
+                  int32_t head_dim, int32_t block_size, int32_t n_init, int32_t n_local,
+                  int32_t n_topk, int32_t c1_kernel, int32_t c1_stride, int32_t c2_kernel,
+                  int32_t c2_stride, int32_t pool_kernel, int32_t pool_stride,
+                  int32_t pool_pad, float softmax_scale, void* workspace,
+                  size_t* workspace_bytes, int32_t* block_idx, void* stream, bool unfused) {
   int rc = common_seq_checks(batch, max_seqlen_q, max_seqlen_k, rows_q, 0);
   if (rc) return rc;
   REQUIRE(c1_rows >= 0 && c2_rows >= 0, INFLLMV2_EINVAL, "negative compressed row count");
@@ -351,7 +369,7 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   REQUIRE(std::isfinite(softmax_scale) && softmax_scale > 0.f, INFLLMV2_EINVAL, "softmax_scale must be finite and > 0");
   REQUIRE(ceil_div(max_seqlen_k, kBlock) <= kMaxBlocks, INFLLMV2_EUNSUPPORTED,
           "more than %d blocks per sequence", kMaxBlocks);
-  const SelectLayout L = select_layout(rows_q, batch, max_seqlen_q, h_q, h_kv, max_seqlen_k);
+  const SelectLayout L = select_layout(rows_q, batch, max_seqlen_q, h_q, h_kv, max_seqlen_k, unfused);
   bool query = false;
   rc = workspace_check(workspace, workspace_bytes, L.total, &query);
   if (rc || query) return rc;
@@ -384,6 +402,10 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   sa.batch = batch;
   sa.splits = L.splits;
   sa.part = L.splits > 0 ? reinterpret_cast<float*>(ws + L.lse_bytes + L.bs_bytes) : nullptr;
+  sa.sc1 = unfused ? reinterpret_cast<float*>(ws + L.lse_bytes + L.bs_bytes + L.part_bytes) : nullptr;
+  sa.sc1_ld = L.sc1_ld;
+  sa.chunk0 = 0;
+  sa.chunk_rows = L.chunk_rows;
 
   // Pass 1: exact LSE over the stage-1 keys, or the approximation over the
   // coarse keys.
@@ -404,8 +426,9 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
   p2.c_rows = c1_rows;
   p2.win_kernel = c1_kernel;
   p2.win_stride = c1_stride;
-  rc = hip_status(L.splits > 0 ? launch_score_blocks_split(p2, st)
-                                : launch_score_blocks(p2, batch, max_seqlen_q, st),
+  rc = hip_status(unfused ? launch_score_unfused(p2, batch, max_seqlen_q, st)
+                  : L.splits > 0 ? launch_score_blocks_split(p2, st)
+                                 : launch_score_blocks(p2, batch, max_seqlen_q, st),
                   "score_blocks launch");
   if (rc) return rc;
 
@@ -427,6 +450,47 @@ int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
                   "topk launch");
   if (rc) return rc;
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int infllmv2_select_blocks(const void* q, const void* k_c1, const void* k_c2,
+                           const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                           const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                           const int32_t* cu_c1, const int32_t* cu_c2, int32_t batch,
+                           int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t rows_q,
+                           int64_t c1_rows, int64_t c2_rows, int32_t h_q, int32_t h_kv,
+                           int32_t head_dim, int32_t block_size, int32_t n_init, int32_t n_local,
+                           int32_t n_topk, int32_t c1_kernel, int32_t c1_stride, int32_t c2_kernel,
+                           int32_t c2_stride, int32_t pool_kernel, int32_t pool_stride,
+                           int32_t pool_pad, float softmax_scale, void* workspace,
+                           size_t* workspace_bytes, int32_t* block_idx, void* stream) {
+  return select_common(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, cu_c1, cu_c2,
+                       batch, max_seqlen_q, max_seqlen_k, rows_q, c1_rows, c2_rows, h_q, h_kv,
+                       head_dim, block_size, n_init, n_local, n_topk, c1_kernel, c1_stride,
+                       c2_kernel, c2_stride, pool_kernel, pool_stride, pool_pad, softmax_scale,
+                       workspace, workspace_bytes, block_idx, stream, false);
+}
+
+int infllmv2_select_blocks_unfused(const void* q, const void* k_c1, const void* k_c2,
+                                   const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                                   const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                                   const int32_t* cu_c1, const int32_t* cu_c2, int32_t batch,
+                                   int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t rows_q,
+                                   int64_t c1_rows, int64_t c2_rows, int32_t h_q, int32_t h_kv,
+                                   int32_t head_dim, int32_t block_size, int32_t n_init,
+                                   int32_t n_local, int32_t n_topk, int32_t c1_kernel,
+                                   int32_t c1_stride, int32_t c2_kernel, int32_t c2_stride,
+                                   int32_t pool_kernel, int32_t pool_stride, int32_t pool_pad,
+                                   float softmax_scale, void* workspace, size_t* workspace_bytes,
+                                   int32_t* block_idx, void* stream) {
+  return select_common(q, k_c1, k_c2, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, cu_c1, cu_c2,
+                       batch, max_seqlen_q, max_seqlen_k, rows_q, c1_rows, c2_rows, h_q, h_kv,
+                       head_dim, block_size, n_init, n_local, n_topk, c1_kernel, c1_stride,
+                       c2_kernel, c2_stride, pool_kernel, pool_stride, pool_pad, softmax_scale,
+                       workspace, workspace_bytes, block_idx, stream, true);
 }
 
 int infllmv2_sparse_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,

@@ -49,6 +49,11 @@ struct ScoreArgs {
   int batch;                // split path: sequences (row -> sequence search)
   int splits;               // split path: window ranges per (row, KV group)
   float* part;              // split path: LSE partials [rows_q, h_kv, splits, 16, 2]
+  // Unfused baseline only: per-head probabilities of one chunk of query rows,
+  // [batch, chunk_rows, h_kv, G, sc1_ld] fp32 (windows at their absolute index).
+  float* sc1;
+  int64_t sc1_ld;
+  int chunk0, chunk_rows;
 };
 
 struct TopkArgs {
@@ -86,6 +91,10 @@ hipError_t launch_compress(const CompressArgs& a, int batch, int max_windows, hi
 hipError_t launch_transpose_v(const TransposeArgs& a, hipStream_t st);
 hipError_t launch_score_lse(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st);
 hipError_t launch_score_blocks(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st);
+// Unfused baseline of pass 2 (the fusion ablation): per chunk of
+// a.chunk_rows query rows, every head's probabilities to a.sc1, then the
+// group sum and max pool from there into a.bs.
+hipError_t launch_score_unfused(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st);
 // Split-K scoring for launches with few query tiles (decode): pass 1 writes
 // per-range (max, sum) partials of the LSE, pass 2 merges them and writes the
 // block scores of its range.

@@ -101,7 +101,8 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
   const int g = blockIdx.y;
   const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
   const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
-  const int i0 = blockIdx.x * kQT;
+  // PASS 3 (unfused baseline) runs over one chunk of query rows at a time.
+  const int i0 = (PASS == 3 ? a.chunk0 : 0) + blockIdx.x * kQT;
   if (i0 >= rq.len) return;
   const int pos0 = rk.len - rq.len;
   const int nq = min(kQT, rq.len - i0);
@@ -156,7 +157,7 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
       if (hv) v = ldg16(a.q + (trow[k] * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
       qa[k][ks] = as_bf16x8(v);
     }
-    if (PASS == 2) {
+    if (PASS >= 2) {
       // Loads at clamped addresses first, the conditions after, so the four
       // loads are in flight together.
       float lraw[4];
@@ -356,6 +357,25 @@ __device__ __forceinline__ void score_body(const ScoreArgs& a, uint8_t* lds) {
       for (int k = 0; k < kTPW; ++k)
 #pragma unroll
         for (int r = 0; r < 4; ++r) ssum[k][r] = ns[k][r];
+    } else if (PASS == 3) {
+      // Unfused baseline: every head's probability of every visible window
+      // goes to the S_C1 chunk buffer [batch][chunk_rows][h_kv][G][sc1_ld].
+      float* dst[kTPW];
+#pragma unroll
+      for (int k = 0; k < kTPW; ++k)
+        dst[k] = a.sc1 + (((int64_t)s * a.chunk_rows + (i0 - a.chunk0) + wave * kTPW + k) * a.h_kv + g) *
+                             a.G * a.sc1_ld;
+      walk(cur, [&](floatx4 (&acc)[kTPW], int ct) {
+        const int j = jt + 16 * ct + c16;
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k) {
+          if (need[k] && j < nv[k]) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (4 * q4 + r < a.G) dst[k][(int64_t)(4 * q4 + r) * a.sc1_ld + j] = fast_exp2(fmaf(acc[k][r], a.c, -Lc[k][r]));
+          }
+        }
+      });
     } else {
       float sct[kTPW][kCT];
       if (full) {
@@ -441,6 +461,53 @@ __global__ __launch_bounds__(256, 2) void score_blocks_kernel(ScoreArgs a) {
   score_body<2>(a, lds);
 }
 
+// Unfused baseline of pass 2 (the layout the fused kernel avoids): the
+// per-head probabilities of one chunk of query rows reach HBM.
+__global__ __launch_bounds__(256, 2) void score_probs_kernel(ScoreArgs a) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kWT * 256];
+  score_body<3>(a, lds);
+}
+
+// Unfused baseline, second step: one wave per (query row of the chunk, KV
+// group) reads the G heads' probabilities of each candidate window from the
+// chunk buffer, sums them (the group sum) and max-pools the sums into block
+// scores, written in the same layout as the fused kernel's.
+__global__ __launch_bounds__(256) void group_pool_kernel(ScoreArgs a) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int s = blockIdx.z, g = blockIdx.y;
+  const int ic = blockIdx.x * 4 + wave;              // row within the chunk
+  const int i = a.chunk0 + ic;
+  const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
+  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
+  if (ic >= a.chunk_rows || i >= rq.len) return;
+  const int t = rk.len - rq.len + i;
+  const int64_t row = (int64_t)rq.start + i;
+  if (t < 0 || row >= a.rows_q) return;
+  const int bt = t / kBlock;
+  if (bt - a.n_local - a.n_init + 1 <= a.n_topk) return;   // keeps every candidate
+  const int nwin = rk.len >= a.win_kernel ? (rk.len - a.win_kernel) / a.win_stride + 1 : 0;
+  const int nv = n_visible(t, a.win_kernel, a.win_stride, nwin);
+  const int b_hi = (int)min((int64_t)(bt - a.n_local), a.bs_ld - 1);
+  const float* src = a.sc1 + (((int64_t)s * a.chunk_rows + ic) * a.h_kv + g) * a.G * a.sc1_ld;
+  float* bsr = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld;
+  int carry = 0;
+  const int j_hi = 4 * b_hi + 4;
+  for (int j0 = max(0, 4 * a.n_init - 1) & ~63; j0 < j_hi; j0 += 64) {
+    const int j = j0 + lane;
+    float S = 0.f;
+    if (j < nv && j < a.sc1_ld)
+      for (int h = 0; h < a.G; ++h) S += src[(int64_t)h * a.sc1_ld + j];
+    // Non-negative sums are ordered as their bit patterns: integer maxima.
+    const int si = __float_as_int(S);
+    const int q1 = max(si, __builtin_amdgcn_update_dpp(0, si, 0xB1, 0xF, 0xF, true));   // quad_perm 1,0,3,2
+    const int qm = max(q1, __builtin_amdgcn_update_dpp(0, q1, 0x4E, 0xF, 0xF, true));   // quad_perm 2,3,0,1
+    const int prev = __builtin_amdgcn_update_dpp(carry, si, 0x138, 0xF, 0xF, false);    // wave_shr:1
+    carry = __builtin_amdgcn_readlane(si, 63);
+    const int b = (j0 >> 2) + (lane >> 2);
+    if ((lane & 3) == 0 && b >= a.n_init && b <= b_hi) bsr[b] = __int_as_float(max(qm, prev));
+  }
+}
+
 }  // namespace
 
 hipError_t launch_score_lse(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st) {
@@ -453,6 +520,21 @@ hipError_t launch_score_blocks(const ScoreArgs& a, int batch, int max_seqlen_q, 
   dim3 grid((max_seqlen_q + kQT - 1) / kQT, a.h_kv, batch);
   hipLaunchKernelGGL(score_blocks_kernel, grid, dim3(256), 0, st, a);
   return hipGetLastError();
+}
+
+hipError_t launch_score_unfused(const ScoreArgs& a, int batch, int max_seqlen_q, hipStream_t st) {
+  for (int c0 = 0; c0 < max_seqlen_q; c0 += a.chunk_rows) {
+    ScoreArgs b = a;
+    b.chunk0 = c0;
+    const int rows = min(a.chunk_rows, max_seqlen_q - c0);
+    hipLaunchKernelGGL(score_probs_kernel, dim3((rows + kQT - 1) / kQT, a.h_kv, batch), dim3(256), 0, st, b);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(group_pool_kernel, dim3((rows + 3) / 4, a.h_kv, batch), dim3(256), 0, st, b);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace infllmv2

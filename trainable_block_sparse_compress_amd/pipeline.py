@@ -58,8 +58,9 @@ class SparsePlan:
     allocated inside ``run``."""
 
     def __init__(self, q_starts, q_lens, k_starts, k_lens, rows_q, h_q, h_kv, cfg: SparseConfig,
-                 device="cuda", d=128):
+                 device="cuda", d=128, unfused_select=False):
         self.cfg = cfg
+        self.unfused_select = unfused_select   # the fusion-ablation baseline of the selection
         self.batch = len(q_lens)
         self.max_q = max(q_lens) if q_lens else 0
         self.max_k = max(k_lens) if k_lens else 0
@@ -86,7 +87,8 @@ class SparsePlan:
             self.cu_c2, self.kc2 = None, None
         self.block_idx = torch.empty((h_kv, rows_q, cfg.n_sel), dtype=torch.int32, device=device)
         ws1 = B.select_blocks_workspace(rows_q, h_q, h_kv, self.max_q, self.max_k, cfg.n_init,
-                                        cfg.n_local, cfg.n_topk, self.approx, batch=self.batch)
+                                        cfg.n_local, cfg.n_topk, self.approx, batch=self.batch,
+                                        unfused=unfused_select)
         ws2 = B.attn_workspace(h_q, h_kv, self.batch, self.max_q, self.max_k, rows_q,
                                n_sel=cfg.n_sel, n_init=cfg.n_init, n_local=cfg.n_local)
         self.ws_select = torch.empty(ws1, dtype=torch.uint8, device=device)
@@ -102,7 +104,8 @@ class SparsePlan:
 
     def select(self, q):
         c = self.cfg
-        B.select_blocks(q, self.kc1, self.kc2, self.cu_q, self.used_q, self.cu_k, self.used_k,
+        fn = B.select_blocks_unfused if self.unfused_select else B.select_blocks
+        fn(q, self.kc1, self.kc2, self.cu_q, self.used_q, self.cu_k, self.used_k,
                         self.cu_c1, self.cu_c2, self.batch, self.max_q, self.max_k, c.n_init,
                         c.n_local, c.n_topk, c.scale(self.d), self.block_idx, self.ws_select,
                         block_size=c.block_size, c1=c.c1, c2=c.c2, pool=c.pool)
