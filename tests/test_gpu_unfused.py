@@ -61,7 +61,7 @@ def test_unfused_select_32k_against_oracle_and_fused(lib):
     pos = sample_positions(n, 64, seed=2, must=(6143, 6144, 16383, 16384, 20000 - 1))
     say(f"  {_check_rows(inp, [n], h_q, h_kv, p, idx_u, lse_u, [pos], plan_u)}")
     plan_f, idx_f, lse_f = _select(inp, [n], h_q, h_kv, p, False)
-    assert np.array_equal(lse_u, lse_f)
+    assert np.array_equal(lse_u[:, 96 * 64:], lse_f[:, 96 * 64:])   # pass 1 is shared (rows with scores)
     rows = list(range(96 * 64, n, 7))
     bu, bf = _block_scores(plan_u, h_q, n, rows), _block_scores(plan_f, h_q, n, rows)
     worst = 0.0
