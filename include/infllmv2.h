@@ -227,6 +227,36 @@ int infllmv2_sparse_attn(const void* q, const void* k, const void* v,
                          void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * infllmv2_sparse_attn_noalloc — infllmv2_sparse_attn for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, layouts, kernels and
+ * results as infllmv2_sparse_attn, without the workspace: the scratch that
+ * call would take from the workspace (the transposed V when v_seq_stride ==
+ * 0; the split-K partials of launches with few query tiles, i.e. decode)
+ * lives in a static device array of 64 MiB (67108864 bytes) that every GPU
+ * the library runs on holds until the process ends.  A call whose scratch
+ * would exceed it returns INFLLMV2_EUNSUPPORTED (message in
+ * infllmv2_last_error) before any HIP call; e.g. the transposed V of one
+ * 131072-token sequence with 2 KV heads is exactly 64 MiB, and decode at
+ * batch 16 with a 128K cache needs 4.3 MB of partials.  The function
+ * allocates, frees and synchronises nothing; the first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress).  Calls on
+ * one GPU share its array and keep the previous call's contents: calls
+ * that overlap on one GPU (different streams, or host threads) race and
+ * must be ordered by the caller.  The scratch needs no clearing (every
+ * element a kernel reads was written by the same call).
+ */
+int infllmv2_sparse_attn_noalloc(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                                 const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                                 int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int64_t rows_q, int64_t rows_k,
+                                 int32_t h_q, int32_t h_kv, int32_t head_dim, int32_t block_size,
+                                 const int32_t* block_idx, int32_t n_sel, int32_t n_init, int32_t n_local,
+                                 float softmax_scale, int64_t v_seq_stride,
+                                 void* out, float* lse_out, void* stream);
+
+/*
  * infllmv2_dense_attn — plain causal attention over every key <= position,
  * the path short sequences take (reading notes section "Dense-Sparse
  * Switchable Attention"; dtcms.com article section 二.2.c: dense below a

@@ -265,3 +265,16 @@ def test_binding_rejects_mismatched_shapes():
     with pytest.raises(B.InfLLMv2Error):
         B.sparse_attn_bwd(q, k, k, q, torch.zeros((4, 100)), q, cu, None, cu, None, 1, 100, 100, idx,
                           1, 2, 0.1, q, k, torch.zeros((100, 2, 64), dtype=bf), None)
+
+
+def test_noalloc_attention_rejects_scratch_above_its_maximum(lib):
+    """infllmv2_sparse_attn_noalloc refuses, before any HIP call, a call
+    whose scratch (here the transposed V of 200000 keys x 2 KV heads, 97.7 MB)
+    exceeds its 64 MiB static array; without a GPU, a call that fits goes on
+    to the pointer checks (EINVAL for the NULL tensors)."""
+    fn = lib.infllmv2_sparse_attn_noalloc
+    args = [None] * 7
+    rc = fn(*args, 1, 200000, 200000, 200000, 200000, 32, 2, 128, 64, None, 8, 1, 2, 0.1, 0, None, None, None)
+    assert rc == EUNSUP and b"static maximum" in lib.infllmv2_last_error()
+    rc = fn(*args, 1, 1000, 1000, 1000, 1000, 32, 2, 128, 64, None, 8, 1, 2, 0.1, 0, None, None, None)
+    assert rc == EINVAL

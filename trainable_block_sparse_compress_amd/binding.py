@@ -15,7 +15,8 @@ import torch
 
 __all__ = [
     "InfLLMv2Error", "load", "library_path", "version", "compress_k", "select_blocks",
-    "select_blocks_workspace", "select_blocks_unfused", "sparse_attn", "dense_attn", "attn_workspace",
+    "select_blocks_workspace", "select_blocks_unfused", "sparse_attn", "sparse_attn_noalloc",
+    "dense_attn", "attn_workspace",
     "sparse_attn_bwd", "attn_bwd_workspace",
 ]
 
@@ -40,6 +41,8 @@ _SIGS = {
                                        _I32, _I32, _I32, _I32, _I32, _I32, _F, _P, _SZP, _P, _P],
     "infllmv2_sparse_attn": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32, _I32,
                              _I32, _I32, _P, _I32, _I32, _I32, _F, _I64, _P, _P, _P, _SZP, _P],
+    "infllmv2_sparse_attn_noalloc": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32,
+                                     _I32, _I32, _I32, _P, _I32, _I32, _I32, _F, _I64, _P, _P, _P],
     "infllmv2_dense_attn": [_P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64, _I64, _I32, _I32,
                             _I32, _F, _I64, _P, _P, _P, _SZP, _P],
     "infllmv2_sparse_attn_bwd": [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I64,
@@ -251,6 +254,25 @@ def sparse_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch
         _i32(seqused_k, "seqused_k"), batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, h_q,
         h_kv, d, block_size, _i32(block_idx, "block_idx"), n_sel, n_init, n_local, softmax_scale,
         v_seq_stride, _bf16(out, "out"), _ptr(lse), ws, ws_bytes, _stream()))
+
+
+def sparse_attn_noalloc(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch,
+                        max_seqlen_q, max_seqlen_k, block_idx, n_init, n_local, softmax_scale, out,
+                        lse=None, v_seq_stride=0, block_size=64):
+    """sparse_attn through infllmv2_sparse_attn_noalloc: no workspace, the
+    library's static per-GPU scratch instead (at most 64 MiB)."""
+    rows_q, h_q, d = q.shape
+    rows_k, h_kv, _ = k.shape
+    n_sel = block_idx.shape[-1]
+    _attn_shapes(q, k, v, out, lse, v_seq_stride, batch)
+    _shape(block_idx, "block_idx", (h_kv, rows_q, n_sel), torch.int32)
+    _seq_meta(batch, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k)
+    _check(load().infllmv2_sparse_attn_noalloc(
+        _bf16(q, "q"), _bf16(k, "k"), _bf16(v, "v"), _i32(cu_seqlens_q, "cu_seqlens_q"),
+        _i32(seqused_q, "seqused_q"), _i32(cu_seqlens_k, "cu_seqlens_k"),
+        _i32(seqused_k, "seqused_k"), batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k, h_q,
+        h_kv, d, block_size, _i32(block_idx, "block_idx"), n_sel, n_init, n_local, softmax_scale,
+        v_seq_stride, _bf16(out, "out"), _ptr(lse), _stream()))
 
 
 def dense_attn(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch, max_seqlen_q,

@@ -5,6 +5,7 @@
 #include <stdio.h>
 
 #include <cmath>
+#include <mutex>
 #include <string>
 
 #include "infllmv2.h"
@@ -147,13 +148,42 @@ int common_seq_checks(int batch, int max_seqlen_q, int max_seqlen_k, int64_t row
   return INFLLMV2_OK;
 }
 
+// Scratch of infllmv2_sparse_attn_noalloc: one file-scope device array per
+// GPU the library runs on (held until the process ends).  Host code never
+// passes the array's name to a kernel: it uses the device address that
+// hipGetSymbolAddress returns, fetched once per device (with that device
+// current) on the entry point's first call there.
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(INFLLMV2_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+  REQUIRE(dev >= 0 && dev < kMaxDevices, INFLLMV2_EUNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(INFLLMV2_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return INFLLMV2_OK;
+}
+
 int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
                 const int32_t* seqused_q, const int32_t* cu_seqlens_k, const int32_t* seqused_k,
                 int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k, int64_t rows_q,
                 int64_t rows_k, int32_t h_q, int32_t h_kv, int32_t head_dim, const int32_t* block_idx,
                 int32_t n_sel, int32_t n_init, int32_t n_local, float softmax_scale,
                 int64_t v_seq_stride, void* out, float* lse_out, void* workspace,
-                size_t* workspace_bytes, void* stream, bool dense) {
+                size_t* workspace_bytes, void* stream, bool dense, bool noalloc = false) {
   int rc = common_seq_checks(batch, max_seqlen_q, max_seqlen_k, rows_q, rows_k);
   if (rc) return rc;
   REQUIRE(head_dim == kHeadDim, INFLLMV2_EUNSUPPORTED, "head_dim %d unsupported (128 only)", head_dim);
@@ -177,13 +207,23 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_s
   const size_t part_need =
       splits > 0 ? align_up((size_t)rows_q * h_kv * splits * kPartFloats * sizeof(float)) : 0;
   const size_t need = vt_need + part_need;
-  bool query = false;
-  rc = workspace_check(workspace, workspace_bytes, need, &query);
-  if (rc || query) return rc;
+  if (noalloc) {
+    REQUIRE(need <= kNoallocScratchBytes, INFLLMV2_EUNSUPPORTED,
+            "needs %zu bytes of scratch (transposed V %zu, split-K partials %zu), above the static "
+            "maximum of %zu bytes", need, vt_need, part_need, kNoallocScratchBytes);
+  } else {
+    bool query = false;
+    rc = workspace_check(workspace, workspace_bytes, need, &query);
+    if (rc || query) return rc;
+  }
   if (batch == 0 || max_seqlen_q == 0) return ok();
   REQUIRE(rows_q >= 1 && rows_k >= 1, INFLLMV2_EINVAL, "rows_q and rows_k must be >= 1");
   REQUIRE(q && k && v && out && cu_seqlens_q && cu_seqlens_k, INFLLMV2_EINVAL, "null tensor pointer");
   REQUIRE(dense || block_idx, INFLLMV2_EINVAL, "null block_idx");
+  if (noalloc && need > 0) {
+    rc = scratch_address(&workspace);
+    if (rc) return rc;
+  }
   (void)seqused_q;
   (void)seqused_k;
 
@@ -506,6 +546,22 @@ int infllmv2_sparse_attn(const void* q, const void* k, const void* v, const int3
                      max_seqlen_k, rows_q, rows_k, h_q, h_kv, head_dim, block_idx, n_sel, n_init,
                      n_local, softmax_scale, v_seq_stride, out, lse_out, workspace, workspace_bytes,
                      stream, false);
+}
+
+int infllmv2_sparse_attn_noalloc(const void* q, const void* k, const void* v,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_q,
+                                 const int32_t* cu_seqlens_k, const int32_t* seqused_k,
+                                 int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int64_t rows_q, int64_t rows_k, int32_t h_q, int32_t h_kv,
+                                 int32_t head_dim, int32_t block_size, const int32_t* block_idx,
+                                 int32_t n_sel, int32_t n_init, int32_t n_local,
+                                 float softmax_scale, int64_t v_seq_stride, void* out,
+                                 float* lse_out, void* stream) {
+  REQUIRE(block_size == kBlock, INFLLMV2_EUNSUPPORTED, "block_size %d unsupported (64 only)", block_size);
+  return attn_common(q, k, v, cu_seqlens_q, seqused_q, cu_seqlens_k, seqused_k, batch, max_seqlen_q,
+                     max_seqlen_k, rows_q, rows_k, h_q, h_kv, head_dim, block_idx, n_sel, n_init,
+                     n_local, softmax_scale, v_seq_stride, out, lse_out, nullptr, nullptr, stream,
+                     false, true);
 }
 
 int infllmv2_dense_attn(const void* q, const void* k, const void* v, const int32_t* cu_seqlens_q,
