@@ -66,9 +66,12 @@ def source_hash(path):
 
 
 def traffic_from_profile(kernel_src):
-    """HBM bytes per launch from the committed PMC summary, if it was taken
-    on the current kernel source; None otherwise.  The summary covers the
-    default workload (n = 131072, exact LSE) only."""
+    """Bytes per launch between the L2 and the memory side (FETCH_SIZE +
+    WRITE_SIZE, scaled by a plain copy of known size) from the committed PMC
+    summary, if it was taken on the current kernel source; None otherwise.
+    The memory side is HBM or the Infinity Cache in front of it (the
+    counters do not separate them), so this bounds the HBM bytes from above.
+    The summary covers the default workload (n = 131072, exact LSE) only."""
     f = os.path.join(ROOT, "profiles", "attn_kernel_128k_pmc.json")
     if not os.path.exists(f):
         return None
@@ -78,7 +81,7 @@ def traffic_from_profile(kernel_src):
         return None
     if rec.get("source_sha256_16") != source_hash(kernel_src):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("memory_side_bytes_per_launch")
 
 
 def host_cores():

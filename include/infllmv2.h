@@ -131,7 +131,12 @@ int infllmv2_compress_k(const void* k, const int32_t* cu_seqlens_k, const int32_
  *              ascending block ids, -1 padded.  Rows of q outside every
  *              sequence are not written.
  *   workspace  >= *workspace_bytes as returned by a size query with the same
- *              shape arguments (fp32 LSE and block scores)
+ *              shape arguments: fp32 LSE and block scores; launches with few
+ *              query tiles (decode: at most 64 query rows per sequence and
+ *              fewer than 512 tiles of 16 rows per KV group) add per-range
+ *              LSE partials and, with the exact LSE, the logits of the first
+ *              pass (64 bytes per query row, KV group and visible window)
+ *              that the second pass reads back instead of the keys
  *   Supported: (c1_kernel, c1_stride) = (32, 16), (c2_kernel, c2_stride) =
  *   (128, 64), pool (5, 4, 1), n_init + n_local + n_topk >= 1 (>= 2 with
  *   k_c2, so that every row that needs scores sees a coarse window), at most

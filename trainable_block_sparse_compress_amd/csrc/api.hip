@@ -66,6 +66,10 @@ struct SelectLayout {
   int64_t sc1_ld = 0;
   int chunk_rows = 0;
   size_t sc1_bytes = 0;
+  // Split path with the exact LSE: pass 1's stored logits, fp32
+  // [rows_q, h_kv, z_ld, 16], read back by pass 2.
+  int64_t z_ld = 0;
+  size_t z_bytes = 0;
 };
 constexpr size_t kUnfusedChunkBytes = size_t(4) << 30;   // bound of the chunk buffer
 // Workgroups the split scoring path aims for (measured best at batch 16:
@@ -79,7 +83,7 @@ int select_splits(int64_t rows_q, int batch, int max_seqlen_q, int max_seqlen_k,
   return (int)std::max<int64_t>(1, std::min<int64_t>({want, cap, (int64_t)64}));
 }
 SelectLayout select_layout(int64_t rows_q, int batch, int max_seqlen_q, int h_q, int h_kv,
-                           int max_seqlen_k, bool unfused = false) {
+                           int max_seqlen_k, bool unfused, bool approx) {
   SelectLayout L;
   L.bs_ld = round_up(std::max<int64_t>(1, ceil_div(max_seqlen_k, kBlock)), 4);
   L.splits = unfused ? 0 : select_splits(rows_q, batch, max_seqlen_q, max_seqlen_k, h_kv);
@@ -94,7 +98,11 @@ SelectLayout select_layout(int64_t rows_q, int batch, int max_seqlen_q, int h_q,
     L.chunk_rows = (int)std::min<int64_t>(fit, round_up(std::max(1, max_seqlen_q), 16));
     L.sc1_bytes = align_up(per_row * (size_t)L.chunk_rows);
   }
-  L.total = L.lse_bytes + L.bs_bytes + L.part_bytes + L.sc1_bytes;
+  if (L.splits > 0 && !approx) {
+    L.z_ld = round_up(std::max<int64_t>(1, max_seqlen_k >= 32 ? (max_seqlen_k - 32) / 16 + 1 : 1), 16);
+    L.z_bytes = align_up((size_t)rows_q * h_kv * (size_t)L.z_ld * 16 * sizeof(float));
+  }
+  L.total = L.lse_bytes + L.bs_bytes + L.part_bytes + L.sc1_bytes + L.z_bytes;
   return L;
 }
 
@@ -409,7 +417,7 @@ int select_common(const void* q, const void* k_c1, const void* k_c2,
   REQUIRE(std::isfinite(softmax_scale) && softmax_scale > 0.f, INFLLMV2_EINVAL, "softmax_scale must be finite and > 0");
   REQUIRE(ceil_div(max_seqlen_k, kBlock) <= kMaxBlocks, INFLLMV2_EUNSUPPORTED,
           "more than %d blocks per sequence", kMaxBlocks);
-  const SelectLayout L = select_layout(rows_q, batch, max_seqlen_q, h_q, h_kv, max_seqlen_k, unfused);
+  const SelectLayout L = select_layout(rows_q, batch, max_seqlen_q, h_q, h_kv, max_seqlen_k, unfused, approx);
   bool query = false;
   rc = workspace_check(workspace, workspace_bytes, L.total, &query);
   if (rc || query) return rc;
@@ -446,6 +454,9 @@ int select_common(const void* q, const void* k_c1, const void* k_c2,
   sa.sc1_ld = L.sc1_ld;
   sa.chunk0 = 0;
   sa.chunk_rows = L.chunk_rows;
+  sa.zbuf = L.z_bytes > 0 ? reinterpret_cast<float*>(ws + L.lse_bytes + L.bs_bytes + L.part_bytes + L.sc1_bytes)
+                          : nullptr;
+  sa.z_ld = L.z_ld;
 
   // Pass 1: exact LSE over the stage-1 keys, or the approximation over the
   // coarse keys.
@@ -467,6 +478,7 @@ int select_common(const void* q, const void* k_c1, const void* k_c2,
   p2.win_kernel = c1_kernel;
   p2.win_stride = c1_stride;
   rc = hip_status(unfused ? launch_score_unfused(p2, batch, max_seqlen_q, st)
+                  : L.z_bytes > 0 ? launch_score_blocks_z_split(p2, st)
                   : L.splits > 0 ? launch_score_blocks_split(p2, st)
                                  : launch_score_blocks(p2, batch, max_seqlen_q, st),
                   "score_blocks launch");

@@ -49,6 +49,11 @@ struct ScoreArgs {
   int batch;                // split path: sequences (row -> sequence search)
   int splits;               // split path: window ranges per (row, KV group)
   float* part;              // split path: LSE partials [rows_q, h_kv, splits, 16, 2]
+  // Split path, exact LSE: pass 1 also stores every logit (scaled by c, log2
+  // units) of the row's visible windows, [rows_q, h_kv, z_ld, 16] fp32, so that
+  // pass 2 reads them instead of the keys.
+  float* zbuf;
+  int64_t z_ld;
   // Unfused baseline only: per-head probabilities of one chunk of query rows,
   // [batch, chunk_rows, h_kv, G, sc1_ld] fp32 (windows at their absolute index).
   float* sc1;
@@ -100,6 +105,8 @@ hipError_t launch_score_unfused(const ScoreArgs& a, int batch, int max_seqlen_q,
 // block scores of its range.
 hipError_t launch_score_lse_split(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_score_blocks_split(const ScoreArgs& a, hipStream_t st);
+// Pass 2 of the split path with the exact LSE, from pass 1's stored logits.
+hipError_t launch_score_blocks_z_split(const ScoreArgs& a, hipStream_t st);
 hipError_t launch_topk(const TopkArgs& a, int batch, int h_kv, int max_seqlen_q, int max_blocks,
                        hipStream_t st);
 // Top-k with a whole workgroup per (query row, KV group), for launches with

@@ -647,6 +647,11 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_lse_split_kernel(
         if (ch + 4 * W < cb) chunk_keys(a, g, r.c0, 16 * (ch + 4 * W), c16, q4, ring[i]);
         const floatx4 acc = chunk_scores(qa, b);
         const bool ok = 16 * ch + c16 < r.nv;
+        if (a.zbuf != nullptr && ok && 16 * ch + c16 < a.z_ld) {
+          // Exact LSE: the logits (log2 units) for the fused pass 2.
+          float* zp = a.zbuf + (((int64_t)row * a.h_kv + g) * a.z_ld + 16 * ch + c16) * 16 + 4 * q4;
+          *reinterpret_cast<floatx4*>(zp) = floatx4{acc[0] * a.c, acc[1] * a.c, acc[2] * a.c, acc[3] * a.c};
+        }
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           if (ok) {
@@ -776,7 +781,96 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_split_kern
   }
 }
 
+// Pass 2 of the split path with the exact LSE: the same work split as
+// score_blocks_split_kernel, but the logits come from pass 1's store (one
+// 16-byte load per lane and window: the lane's four heads), so neither the
+// stage-1 keys nor the matrix cores are needed again.
+__global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_z_split_kernel(ScoreArgs a) {
+  const int sp = blockIdx.x, g = blockIdx.y;
+  const int64_t row = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
+  const int wave = tid >> 6;
+  SplitRow r;
+  if (!split_row(a, row, r)) return;
+  const int b_hi = r.bt - a.n_local;
+  const int cfirst = max(0, 4 * a.n_init - 1) >> 4;
+  const int clast = (4 * b_hi + 3) >> 4;   // inclusive
+  const int nch = clast - cfirst + 1;
+  const int ca0 = cfirst + (int)((int64_t)nch * sp / a.splits);
+  const int cb0 = cfirst + (int)((int64_t)nch * (sp + 1) / a.splits);
+  const int ca = ca0 + (int)((int64_t)(cb0 - ca0) * wave / kSplitScoreWaves);
+  const int cb = ca0 + (int)((int64_t)(cb0 - ca0) * (wave + 1) / kSplitScoreWaves);
+  // Logits of window j, heads 4 q4 .. 4 q4 + 3 (clamped into the visible
+  // windows, which pass 1 wrote; the sums of windows >= nv are dropped).
+  const float* zrow = a.zbuf + ((row * a.h_kv + g) * a.z_ld) * 16 + 4 * q4;
+  const int jmax = max(0, min(r.nv, (int)a.z_ld) - 1);
+  auto zload = [&](int ch) -> floatx4 {
+    const int j = min(16 * ch + c16, jmax);
+    return *reinterpret_cast<const floatx4*>(zrow + (int64_t)j * 16);
+  };
+  floatx4 prevz = floatx4{0.f, 0.f, 0.f, 0.f}, ring[4];
+  if (ca < cb && ca > 0) prevz = zload(ca - 1);
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (ca + i < cb) ring[i] = zload(ca + i);
+  __shared__ float parts[kSplitMaxSplits * 32];
+  {
+    const float* src = a.part + ((int64_t)row * a.h_kv + g) * a.splits * 32;
+    for (int i = tid; i < a.splits * 32; i += 64 * kSplitScoreWaves) parts[i] = src[i];
+  }
+  __syncthreads();
+  if (ca >= cb) return;
+  float Lc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * q4 + i;
+    float mm = -__builtin_inff();
+    for (int p = 0; p < a.splits; ++p) mm = fmaxf(mm, parts[p * 32 + 2 * h]);
+    float ss = 0.f;
+    for (int p = 0; p < a.splits; ++p) {
+      const float m2 = parts[p * 32 + 2 * h];
+      if (m2 > -__builtin_inff()) ss += parts[p * 32 + 2 * h + 1] * fast_exp2((m2 - mm) * a.c);
+    }
+    Lc[i] = (h < a.G && ss > 0.f) ? mm * a.c + __builtin_amdgcn_logf(ss) : __builtin_inff();
+  }
+  auto chunk_sum = [&](int ch, const floatx4& z) -> float {
+    float sum = fast_exp2(z[0] - Lc[0]);
+#pragma unroll
+    for (int i = 1; i < 4; ++i) sum += fast_exp2(z[i] - Lc[i]);
+    sum = sum_x16(sum_x32(sum));   // all heads of the group: lane c16 -> window 16 ch + c16
+    return 16 * ch + c16 < r.nv ? sum : 0.f;
+  };
+  float carry = 0.f;
+  if (ca > 0) carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(chunk_sum(ca - 1, prevz)), 15));
+  float* bsr = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld;
+  for (int base = ca; base < cb; base += 4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int ch = base + i;
+      if (ch < cb) {
+        const floatx4 z = ring[i];
+        if (ch + 4 < cb) ring[i] = zload(ch + 4);   // four ahead
+        const float S = chunk_sum(ch, z);
+        const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));       // quad_perm 1,0,3,2
+        const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));    // quad_perm 2,3,0,1
+        const float prev = dpp_f32<0x138>(carry, S);          // wave_shr:1
+        carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S), 15));
+        if (lane < 16 && (lane & 3) == 0) {
+          const int b = 4 * ch + (lane >> 2);
+          if (b >= a.n_init && b <= b_hi && b < a.bs_ld) bsr[b] = fmaxf(qm, prev);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_score_blocks_z_split(const ScoreArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL(score_blocks_z_split_kernel, dim3(a.splits, a.h_kv, (unsigned)a.rows_q),
+                     dim3(64 * kSplitScoreWaves), 0, st, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_score_lse_split(const ScoreArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(score_lse_split_kernel, dim3(a.splits, a.h_kv, (unsigned)a.rows_q),

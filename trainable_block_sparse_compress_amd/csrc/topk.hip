@@ -295,49 +295,67 @@ __device__ __forceinline__ int wg_exclusive_scan(int v, int* wsum, int& total) {
   return before + incl - v;
 }
 
-template <int PER>
-__global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(TopkArgs a) {
-  __shared__ uint32_t hist[256];
-  __shared__ int wsum[kRowThreads / 64];
-  __shared__ uint32_t ext[3][kRowThreads / 64];
-  __shared__ int pick[2];
-  const int64_t row = blockIdx.x;
-  const int g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// Shared memory of the row selection (one workgroup per (row, KV group)).
+struct RowSelLds {
+  uint32_t hist[256];
+  int wsum[kRowThreads / 64];
+  uint32_t ext[3][kRowThreads / 64];
+  int pick[2];
+};
+
+// Row setup shared by the row kernels: false when the row is outside every
+// sequence; otherwise the row's last block and candidate range, and rows
+// that keep every candidate (or take no top-k) are emitted here (done = true).
+struct RowSetup {
+  int bt, lo, hi, nc, n_sel;
+  int32_t* out;
+  bool done;
+};
+__device__ __forceinline__ bool row_setup(const TopkArgs& a, int64_t row, int g, int tid, RowSetup& r) {
   const int s = seq_of_row_t(a, row);
-  if (s < 0) return;
+  if (s < 0) return false;
   const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
   const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
   const int t = rk.len - rq.len + (int)(row - rq.start);
-  if (t < 0) return;
-  const int bt = t / kBlock;
-  const int n_sel = a.n_init + a.n_local + a.n_topk;
-  int32_t* out = a.idx + ((int64_t)g * a.rows_q + row) * n_sel;
-  const int lo = a.n_init;
-  const int hi = (int)min((int64_t)(bt - a.n_local), a.bs_ld - 1);
-  const int nc = hi - lo + 1;
-  if (nc <= a.n_topk) {
-    for (int e = tid; e < n_sel; e += kRowThreads) out[e] = e <= bt ? e : -1;
-    return;
+  if (t < 0) return false;
+  r.bt = t / kBlock;
+  r.n_sel = a.n_init + a.n_local + a.n_topk;
+  r.out = a.idx + ((int64_t)g * a.rows_q + row) * r.n_sel;
+  r.lo = a.n_init;
+  r.hi = (int)min((int64_t)(r.bt - a.n_local), a.bs_ld - 1);
+  r.nc = r.hi - r.lo + 1;
+  r.done = true;
+  if (r.nc <= a.n_topk) {
+    for (int e = tid; e < r.n_sel; e += kRowThreads) r.out[e] = e <= r.bt ? e : -1;
+    return true;
   }
   if (a.n_topk == 0) {
-    for (int e = tid; e < a.n_init; e += kRowThreads) out[e] = e;
-    for (int r = tid; r < a.n_local; r += kRowThreads) out[a.n_init + r] = bt - a.n_local + 1 + r;
-    return;
+    for (int e = tid; e < a.n_init; e += kRowThreads) r.out[e] = e;
+    for (int q = tid; q < a.n_local; q += kRowThreads) r.out[a.n_init + q] = r.bt - a.n_local + 1 + q;
+    return true;
   }
-  const float* row_bs = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld + lo;
-  uint32_t key[PER];
+  r.done = false;
+  return true;
+}
+
+// Top-n_topk of the row's candidate keys (thread tid holds candidates
+// lo + PER*tid + p as order-preserving keys, bits + 1, 0 = empty) and the
+// emission of init ∪ top-k ∪ local in ascending order.
+template <int PER>
+__device__ __forceinline__ void row_select(const TopkArgs& a, const RowSetup& rs, uint32_t (&key)[PER],
+                                           RowSelLds& sh) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* hist = sh.hist;
+  int* wsum = sh.wsum;
+  auto& ext = sh.ext;
+  int* pick = sh.pick;
+  const int bt = rs.bt, lo = rs.lo;
+  int32_t* out = rs.out;
   uint32_t kmax = 0, kmin = 0xFFFFFFFFu;
-  // All loads first (slots past the row read its last candidate, then are
-  // cleared), so no branch separates a load from the next.
-#pragma unroll
-  for (int p = 0; p < PER; ++p) key[p] = __float_as_uint(row_bs[min(PER * tid + p, nc - 1)]);
 #pragma unroll
   for (int p = 0; p < PER; ++p) {
-    const bool in = PER * tid + p < nc;
-    key[p] = in ? key[p] + 1u : 0u;
-    kmax = in ? max(kmax, key[p]) : kmax;
-    kmin = in ? min(kmin, key[p]) : kmin;
+    kmax = key[p] != 0 ? max(kmax, key[p]) : kmax;
+    kmin = key[p] != 0 ? min(kmin, key[p]) : kmin;
   }
   // Smallest thread maximum: a lower bound of the n_topk-th largest key for
   // n_topk <= kRowThreads (every thread holds a key >= its own maximum);
@@ -447,6 +465,24 @@ __global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(TopkArgs a) {
   }
   const int base = n_init_eff + a.n_topk;
   for (int r = tid; r < a.n_local; r += kRowThreads) out[base + r] = bt - a.n_local + 1 + r;
+}
+
+
+template <int PER>
+__global__ __launch_bounds__(kRowThreads) void topk_rows_kernel(TopkArgs a) {
+  __shared__ RowSelLds sh;
+  const int tid = threadIdx.x;
+  RowSetup rs;
+  if (!row_setup(a, blockIdx.x, blockIdx.y, tid, rs) || rs.done) return;
+  const float* row_bs = a.bs + ((int64_t)blockIdx.y * a.rows_q + blockIdx.x) * a.bs_ld + rs.lo;
+  uint32_t key[PER];
+  // All loads first (slots past the row read its last candidate, then are
+  // cleared), so no branch separates a load from the next.
+#pragma unroll
+  for (int p = 0; p < PER; ++p) key[p] = __float_as_uint(row_bs[min(PER * tid + p, rs.nc - 1)]);
+#pragma unroll
+  for (int p = 0; p < PER; ++p) key[p] = PER * tid + p < rs.nc ? key[p] + 1u : 0u;
+  row_select<PER>(a, rs, key, sh);
 }
 
 }  // namespace
