@@ -120,6 +120,36 @@ def test_dense_attention(lib, lengths, h_q, h_kv):
     say(f"  max abs err {worst:.3e}")
 
 
+@pytest.mark.parametrize("lengths", [[32768], [8192] * 3 + [777]])
+def test_dense_attention_long(lib, lengths):
+    """Dense causal attention of the 32q/2kv layer over one 32K sequence
+    (its tiles are spread over the XCDs in chunks, heaviest first) and over
+    several 8K sequences plus a ragged one (contiguous ranges, heaviest
+    first): sampled rows of every sequence, including the ends of tiles and
+    of the launch order, against the oracle."""
+    say(f"dense long lengths={lengths}")
+    h_q, h_kv = 32, 2
+    inp = D.make_prefill(29, lengths, h_q, h_kv)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    st = _starts(lengths)
+    out = torch.empty_like(q)
+    lse = torch.empty((h_q, q.shape[0]), dtype=torch.float32, device="cuda")
+    P.DensePlan(st, lengths, st, lengths, sum(lengths), h_q, h_kv, P.SparseConfig()).run(q, k, v, out, lse)
+    torch.cuda.synchronize()
+    of, lf = to_f64(out), lse.cpu().numpy()
+    worst = 0.0
+    for s, n in enumerate(lengths):
+        Ks, Vs = R.as_f64(inp.k[st[s]:st[s] + n]), R.as_f64(inp.v[st[s]:st[s] + n])
+        pos = sample_positions(n, 40, seed=s, must=(15, 16, 511, 512, n - 17, n - 16))
+        ref = R.dense_prefill(inp.q[st[s]:st[s] + n], Ks, Vs, h_q // h_kv, 1 / math.sqrt(128), positions=pos)
+        for t in pos:
+            ma, rr = attn_errors(of[st[s] + t], ref[t][0])
+            worst = max(worst, ma)
+            assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (s, t, ma, rr)
+            assert np.abs(lf[:, st[s] + t] - ref[t][1]).max() < 1e-3, (s, t)
+    say(f"  max abs err {worst:.3e}")
+
+
 # ----------------------------------------------------------------------------
 # sparse attention on given block lists (selection noise excluded)
 # ----------------------------------------------------------------------------
