@@ -470,20 +470,8 @@ int select_common(const void* q, const void* k_c1, const void* k_c2,
                   "score_lse launch");
   if (rc) return rc;
 
-  // Pass 2: probabilities, group sum and max pool -> block scores.
-  ScoreArgs p2 = sa;
-  p2.kc = reinterpret_cast<const uint16_t*>(k_c1);
-  p2.cu_c = cu_c1;
-  p2.c_rows = c1_rows;
-  p2.win_kernel = c1_kernel;
-  p2.win_stride = c1_stride;
-  rc = hip_status(unfused ? launch_score_unfused(p2, batch, max_seqlen_q, st)
-                  : L.z_bytes > 0 ? launch_score_blocks_z_split(p2, st)
-                  : L.splits > 0 ? launch_score_blocks_split(p2, st)
-                                 : launch_score_blocks(p2, batch, max_seqlen_q, st),
-                  "score_blocks launch");
-  if (rc) return rc;
-
+  // Pass 2: probabilities, group sum and max pool -> block scores, then the
+  // top-k.
   TopkArgs ta;
   ta.bs = sa.bs;
   ta.bs_ld = L.bs_ld;
@@ -497,8 +485,21 @@ int select_common(const void* q, const void* k_c1, const void* k_c2,
   ta.n_topk = n_topk;
   ta.idx = block_idx;
   ta.batch = batch;
-  rc = hip_status(L.splits > 0 ? launch_topk_rows(ta, h_kv, (int)ceil_div(max_seqlen_k, kBlock), st)
-                               : launch_topk(ta, batch, h_kv, max_seqlen_q, (int)ceil_div(max_seqlen_k, kBlock), st),
+  const int max_blocks = (int)ceil_div(max_seqlen_k, kBlock);
+  ScoreArgs p2 = sa;
+  p2.kc = reinterpret_cast<const uint16_t*>(k_c1);
+  p2.cu_c = cu_c1;
+  p2.c_rows = c1_rows;
+  p2.win_kernel = c1_kernel;
+  p2.win_stride = c1_stride;
+  rc = hip_status(unfused ? launch_score_unfused(p2, batch, max_seqlen_q, st)
+                  : L.z_bytes > 0 ? launch_score_blocks_z_split(p2, st)
+                  : L.splits > 0 ? launch_score_blocks_split(p2, st)
+                                 : launch_score_blocks(p2, batch, max_seqlen_q, st),
+                  "score_blocks launch");
+  if (rc) return rc;
+  rc = hip_status(L.splits > 0 ? launch_topk_rows(ta, h_kv, max_blocks, st)
+                               : launch_topk(ta, batch, h_kv, max_seqlen_q, max_blocks, st),
                   "topk launch");
   if (rc) return rc;
   return ok();

@@ -677,7 +677,9 @@ struct Attn {
 #pragma unroll
     for (int k = 0; k < kTPW; ++k) {
       const float lt = sum_x16(sum_x32(l[k]));
-      if (!tval[k]) continue;
+      // Rows of the sequence placed before its first key attend nothing
+      // (their state is untouched: out = 0, lse = -inf).
+      if (trow[k] - rq.start >= rq.len || trow[k] >= a.rows_q) continue;
       const float inv = lt > 0.f ? 1.f / lt : 0.f;
       if (c16 < a.G) {
         uint16_t* dst = a.out + (trow[k] * a.h_q + g * a.G + c16) * kHeadDim + 4 * q4;
@@ -742,33 +744,39 @@ struct SplitLds {
   float po[kSplitWaves][16 * kHeadDim];
 };
 
-// Sequence holding packed query row `row` (cu_q non-decreasing), or -1.
-__device__ __forceinline__ int seq_of_row(const AttnArgs& a, int64_t row) {
-  int lo = 0, hi = a.batch - 1;
-  if (hi < 0) return -1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cu_q[mid] <= row) lo = mid;
-    else hi = mid - 1;
-  }
-  const SeqRange r = seq_range(a.cu_q, a.used_q, lo);
-  return (row >= r.start && row < (int64_t)r.start + r.len) ? lo : -1;
-}
-
 __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a, int splits, float* part) {
   __shared__ __attribute__((aligned(16))) SplitLds sh;
   const int sp = blockIdx.x, g = blockIdx.y;
   const int64_t row = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int s = seq_of_row(a, row);
-  if (s < 0) return;
-  const SeqRange rq = seq_range(a.cu_q, a.used_q, s);
-  const SeqRange rk = seq_range(a.cu_k, a.used_k, s);
+  const bool dense = a.bidx == nullptr;
+  // The row's list entries and query fragments depend on the row alone: they
+  // are read in the same round as its sequence's metadata.
+  int lv[kSplitMaxSel / kSplitThreads];
+#pragma unroll
+  for (int j = 0; j < kSplitMaxSel / kSplitThreads; ++j) {
+    const int i = tid + kSplitThreads * j;
+    lv[j] = (!dense && i < a.n_sel) ? a.bidx[((int64_t)g * a.rows_q + row) * a.n_sel + i] : -1;
+  }
+  // Query fragments (the group's heads are the 16 MFMA columns, padded).
+  bf16x8 qb[4];
+  {
+    const bool hv = c16 < a.G;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 v = zero16();
+      if (hv) v = ldg16(a.q + (row * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
+      qb[ks] = as_bf16x8(v);
+    }
+  }
+  RowSeq rsq;
+  if (!find_row_seq(a.cu_q, a.used_q, a.cu_k, a.used_k, nullptr, a.batch, row, rsq)) return;
+  const int s = rsq.s;
+  const SeqRange rq = rsq.rq, rk = rsq.rk;
   const int t = rk.len - rq.len + (int)(row - rq.start);
   if (t < 0) return;
   const int bt = t / kBlock;
-  const bool dense = a.bidx == nullptr;
   const int nvt = (int)(a.vt_ld / kBlock);   // blocks inside a V^T row
 
   // The row's block set, ascending and without repeats.
@@ -782,13 +790,11 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     const int nwords = (nbits + 31) >> 5;
     for (int w = tid; w < nwords; w += kSplitThreads) sh.bits[w] = 0u;
     __syncthreads();
-    const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + row) * a.n_sel;
-    const int n_cand = a.n_sel + a.n_init + a.n_local;
-    for (int i = tid; i < n_cand; i += kSplitThreads) {
-      int b;
-      if (i < a.n_sel) b = list[i];
-      else if (i < a.n_sel + a.n_init) b = i - a.n_sel;
-      else b = bt - (i - a.n_sel - a.n_init);
+#pragma unroll
+    for (int j = 0; j < kSplitMaxSel / kSplitThreads; ++j)
+      if (lv[j] >= 0 && lv[j] < nbits) atomicOr(&sh.bits[lv[j] >> 5], 1u << (lv[j] & 31));
+    for (int i = tid; i < a.n_init + a.n_local; i += kSplitThreads) {
+      const int b = i < a.n_init ? i : bt - (i - a.n_init);
       if (b >= 0 && b < nbits) atomicOr(&sh.bits[b >> 5], 1u << (b & 31));
     }
     __syncthreads();
@@ -829,18 +835,6 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
     __syncthreads();
   }
   const int lo = (int)((int64_t)nb * sp / splits), hi = (int)((int64_t)nb * (sp + 1) / splits);
-
-  // Query fragments (the group's heads are the 16 MFMA columns, padded).
-  bf16x8 qb[4];
-  {
-    const bool hv = c16 < a.G;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 v = zero16();
-      if (hv) v = ldg16(a.q + (row * a.h_q + g * a.G + c16) * kHeadDim + 32 * ks + 8 * q4);
-      qb[ks] = as_bf16x8(v);
-    }
-  }
   floatx4 o[8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) o[dt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -962,20 +956,26 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int splits,
   __shared__ float Mh[16], Lh[16];
   const int g = blockIdx.x;
   const int64_t row = blockIdx.y;
-  if (seq_of_row(a, row) < 0) return;
   const int tid = threadIdx.x, h = tid >> 4, d0 = 8 * (tid & 15);
   const float* src = part + ((int64_t)row * a.h_kv + g) * splits * kPartFloats;
-  // Per-split maxima of every head, then each head's weights and sum.
+  // Per-split maxima of every head, then each head's weights and sum (read
+  // in the same round as the row's metadata; a row outside every sequence
+  // has no partials and writes nothing).
   for (int i = tid; i < 16 * splits; i += 256) {
     wt[i >> 4][i & 15] = src[(i >> 4) * kPartFloats + 16 * kHeadDim + 16 + (i & 15)];
     lp[i >> 4][i & 15] = src[(i >> 4) * kPartFloats + 16 * kHeadDim + (i & 15)];
   }
+  RowSeq rsq;
+  if (!find_row_seq(a.cu_q, a.used_q, a.cu_k, a.used_k, nullptr, a.batch, row, rsq)) return;
+  // A row placed before its sequence's first key attends nothing (the split
+  // kernel wrote no partial for it): out = 0, lse = -inf.
+  const int nparts = rsq.rk.len - rsq.rq.len + (int)(row - rsq.rq.start) < 0 ? 0 : splits;
   __syncthreads();
   if (tid < 16) {
     float M = -__builtin_inff();
-    for (int p = 0; p < splits; ++p) M = fmaxf(M, wt[p][tid]);
+    for (int p = 0; p < nparts; ++p) M = fmaxf(M, wt[p][tid]);
     float L = 0.f;
-    for (int p = 0; p < splits; ++p) {
+    for (int p = 0; p < nparts; ++p) {
       const float w = fast_exp2((wt[p][tid] - M) * a.c);
       wt[p][tid] = w;
       L += w * lp[p][tid];
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a, int splits,
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.f;
 #pragma unroll 4
-  for (int p = 0; p < splits; ++p) {
+  for (int p = 0; p < nparts; ++p) {
     const float* pp = src + p * kPartFloats + h * kHeadDim + d0;
     const floatx4 x0 = *reinterpret_cast<const floatx4*>(pp);
     const floatx4 x1 = *reinterpret_cast<const floatx4*>(pp + 4);

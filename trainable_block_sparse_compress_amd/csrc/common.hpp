@@ -91,4 +91,54 @@ __device__ __forceinline__ SeqRange seq_range(const int32_t* cu, const int32_t* 
   return r;
 }
 
+// Sequence of packed query row `row`, with its query and key ranges and (if
+// cu_c is given) its first compressed row.  cu_q is non-decreasing with
+// batch + 1 entries; the row's sequence is the last one whose query start is
+// <= row.  Up to 64 sequences this costs one round of loads: lane i reads
+// sequence i's entries, a ballot finds the sequence and its lane's values
+// are broadcast.  Larger batches binary-search.  Every lane of the wave
+// calls it with the same row.  False when the row lies in no sequence.
+struct RowSeq {
+  int s;
+  SeqRange rq, rk;
+  int c0;
+};
+__device__ __forceinline__ bool find_row_seq(const int32_t* cu_q, const int32_t* used_q, const int32_t* cu_k,
+                                             const int32_t* used_k, const int32_t* cu_c, int batch, int64_t row,
+                                             RowSeq& r) {
+  if (batch <= 0) return false;
+  if (batch <= 64) {
+    const int lane = __lane_id();
+    const bool in = lane < batch;
+    const int i = in ? lane : 0;
+    const int qs = cu_q[i];
+    const int ql = used_q ? used_q[i] : cu_q[i + 1] - qs;
+    const int ks = cu_k[i];
+    const int kl = used_k ? used_k[i] : cu_k[i + 1] - ks;
+    const int cc = cu_c ? cu_c[i] : 0;
+    const uint64_t le = __ballot(in && (int64_t)qs <= row);
+    const int s = le ? 63 - __clzll((long long)le) : 0;
+    r.s = s;
+    r.rq.start = __builtin_amdgcn_readlane(qs, s);
+    r.rq.len = __builtin_amdgcn_readlane(ql, s);
+    r.rk.start = __builtin_amdgcn_readlane(ks, s);
+    r.rk.len = __builtin_amdgcn_readlane(kl, s);
+    r.c0 = __builtin_amdgcn_readlane(cc, s);
+    if (r.rq.start < 0 || r.rq.len < 0) r.rq = SeqRange{0, 0};
+    if (r.rk.start < 0 || r.rk.len < 0) r.rk = SeqRange{0, 0};
+  } else {
+    int lo = 0, hi = batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu_q[mid] <= row) lo = mid;
+      else hi = mid - 1;
+    }
+    r.s = lo;
+    r.rq = seq_range(cu_q, used_q, lo);
+    r.rk = seq_range(cu_k, used_k, lo);
+    r.c0 = cu_c ? cu_c[lo] : 0;
+  }
+  return row >= r.rq.start && row < (int64_t)r.rq.start + r.rq.len;
+}
+
 }  // namespace infllmv2

@@ -556,19 +556,8 @@ namespace infllmv2 {
 namespace {
 
 constexpr int kSplitScoreWaves = 4;
-constexpr int kSplitDepth = 4;   // chunks each wave keeps in flight on the split path
-
-__device__ __forceinline__ int seq_of_row_s(const ScoreArgs& a, int64_t row) {
-  int lo = 0, hi = a.batch - 1;
-  if (hi < 0) return -1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (a.cu_q[mid] <= row) lo = mid;
-    else hi = mid - 1;
-  }
-  const SeqRange r = seq_range(a.cu_q, a.used_q, lo);
-  return (row >= r.start && row < (int64_t)r.start + r.len) ? lo : -1;
-}
+constexpr int kSplitDepth = 8;   // key chunks each wave keeps in flight in split pass 1
+constexpr int kZDepth = 16;      // logit chunks each wave keeps in flight in split pass 2
 
 // Row setup shared by both passes; false when the row needs no scores.
 struct SplitRow {
@@ -576,17 +565,17 @@ struct SplitRow {
   int64_t c0;
 };
 __device__ __forceinline__ bool split_row(const ScoreArgs& a, int64_t row, SplitRow& r) {
-  r.s = seq_of_row_s(a, row);
-  if (r.s < 0) return false;
-  const SeqRange rq = seq_range(a.cu_q, a.used_q, r.s);
-  const SeqRange rk = seq_range(a.cu_k, a.used_k, r.s);
+  RowSeq rsq;
+  if (!find_row_seq(a.cu_q, a.used_q, a.cu_k, a.used_k, a.cu_c, a.batch, row, rsq)) return false;
+  r.s = rsq.s;
+  const SeqRange rq = rsq.rq, rk = rsq.rk;
   r.t = rk.len - rq.len + (int)(row - rq.start);
   if (r.t < 0) return false;
   r.bt = r.t / kBlock;
   if (r.bt - a.n_local - a.n_init + 1 <= a.n_topk) return false;   // keeps every candidate
   const int nwin = rk.len >= a.win_kernel ? (rk.len - a.win_kernel) / a.win_stride + 1 : 0;
   r.nv = n_visible(r.t, a.win_kernel, a.win_stride, nwin);
-  r.c0 = a.cu_c[r.s];
+  r.c0 = rsq.c0;
   return r.c0 >= 0 && r.c0 < a.c_rows;   // inconsistent metadata: row skipped
 }
 
@@ -624,10 +613,10 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_lse_split_kernel(
   const int64_t row = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
   const int wave = tid >> 6;
+  bf16x8 qa[4];
+  load_q(a, row, g, c16, q4, qa);   // in the same round as the row's metadata
   SplitRow r;
   if (!split_row(a, row, r)) return;
-  bf16x8 qa[4];
-  load_q(a, row, g, c16, q4, qa);
   const int nch = (r.nv + 15) >> 4;
   const int ca = (int)((int64_t)nch * sp / a.splits), cb = (int)((int64_t)nch * (sp + 1) / a.splits);
   float m[4], sm[4];
@@ -636,7 +625,7 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_lse_split_kernel(
     m[i] = -__builtin_inff();
     sm[i] = 0.f;
   }
-  // This wave's chunks: ca + wave, ca + wave + 4, ...; four of them in flight.
+  // This wave's chunks: ca + wave, ca + wave + W, ...; DP of them in flight.
   constexpr int W = kSplitScoreWaves;
   constexpr int DP = kSplitDepth;
   bf16x8 ring[DP][4];
@@ -795,6 +784,13 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_z_split_ke
   const int64_t row = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, q4 = lane >> 4, c16 = lane & 15;
   const int wave = tid >> 6;
+  // The row's LSE partials, fetched by the whole workgroup in the same round
+  // as the row's metadata.
+  __shared__ float parts[kSplitMaxSplits * 32];
+  {
+    const float* src = a.part + ((int64_t)row * a.h_kv + g) * a.splits * 32;
+    for (int i = tid; i < a.splits * 32; i += 64 * kSplitScoreWaves) parts[i] = src[i];
+  }
   SplitRow r;
   if (!split_row(a, row, r)) return;
   const int b_hi = r.bt - a.n_local;
@@ -813,16 +809,11 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_z_split_ke
     const int j = min(16 * ch + c16, jmax);
     return *reinterpret_cast<const floatx4*>(zrow + (int64_t)j * 16);
   };
-  floatx4 prevz = floatx4{0.f, 0.f, 0.f, 0.f}, ring[kSplitDepth];
+  floatx4 prevz = floatx4{0.f, 0.f, 0.f, 0.f}, ring[kZDepth];
   if (ca < cb && ca > 0) prevz = zload(ca - 1);
 #pragma unroll
-  for (int i = 0; i < kSplitDepth; ++i)
+  for (int i = 0; i < kZDepth; ++i)
     if (ca + i < cb) ring[i] = zload(ca + i);
-  __shared__ float parts[kSplitMaxSplits * 32];
-  {
-    const float* src = a.part + ((int64_t)row * a.h_kv + g) * a.splits * 32;
-    for (int i = tid; i < a.splits * 32; i += 64 * kSplitScoreWaves) parts[i] = src[i];
-  }
   __syncthreads();
   if (ca >= cb) return;
   float Lc[4];
@@ -848,13 +839,13 @@ __global__ __launch_bounds__(64 * kSplitScoreWaves) void score_blocks_z_split_ke
   float carry = 0.f;
   if (ca > 0) carry = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(chunk_sum(ca - 1, prevz)), 15));
   float* bsr = a.bs + ((int64_t)g * a.rows_q + row) * a.bs_ld;
-  for (int base = ca; base < cb; base += kSplitDepth) {
+  for (int base = ca; base < cb; base += kZDepth) {
 #pragma unroll
-    for (int i = 0; i < kSplitDepth; ++i) {
+    for (int i = 0; i < kZDepth; ++i) {
       const int ch = base + i;
       if (ch < cb) {
         const floatx4 z = ring[i];
-        if (ch + kSplitDepth < cb) ring[i] = zload(ch + kSplitDepth);   // kSplitDepth ahead
+        if (ch + kZDepth < cb) ring[i] = zload(ch + kZDepth);   // kZDepth ahead
         const float S = chunk_sum(ch, z);
         const float q1 = fmaxf(S, dpp_f32<0xB1>(S, S));       // quad_perm 1,0,3,2
         const float qm = fmaxf(q1, dpp_f32<0x4E>(q1, q1));    // quad_perm 2,3,0,1
