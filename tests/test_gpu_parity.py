@@ -276,6 +276,67 @@ def test_split_path_short_queries(lib, h_q, h_kv):
                 assert np.abs(lf[:, qst[s] + i] - l_ref).max() < 1e-3, (dense, s, i)
 
 
+@pytest.mark.parametrize("klens,qlens", [
+    ([40, 700], [50, 3]),          # few query tiles: the split-K kernels
+    ([100, 3000], [300, 3000]),    # the tile kernel
+])
+def test_rows_before_first_key(lib, klens, qlens):
+    """A sequence with more query rows than keys places its first rows
+    before the first key (position t = len_k - len_q + i < 0): such a row
+    attends no key, so the entry points give out = 0 and lse = -inf (the
+    contract of infllmv2.h); the other rows match the oracle.  Sparse (local
+    blocks only, empty lists) and dense, on both kernel paths."""
+    h_q, h_kv = 32, 2
+    say(f"rows before the first key klens={klens} qlens={qlens}")
+    iq = D.make_prefill(41, qlens, h_q, h_kv)
+    ik = D.make_prefill(42, klens, h_q, h_kv)
+    q, k, v = to_dev(iq.q), to_dev(ik.k), to_dev(ik.v)
+    qst, kst = _starts(qlens), _starts(klens)
+    rows = sum(qlens)
+    p = R.Params(n_init=0, n_local=2, n_topk=1)
+    idx = torch.full((h_kv, rows, 1), -1, dtype=torch.int32, device="cuda")
+    scale = 1 / math.sqrt(128)
+    args = (i32(qst), i32(qlens), i32(kst), i32(klens), 2, max(qlens), max(klens))
+    for dense in (False, True):
+        ws = torch.empty(max(1, B.attn_workspace(h_q, h_kv, 2, max(qlens), max(klens), rows,
+                                                 n_sel=0 if dense else 1, n_init=0, n_local=2)),
+                         dtype=torch.uint8, device="cuda")
+        out = torch.full_like(q, float("nan"))
+        lse = torch.full((h_q, rows), float("nan"), dtype=torch.float32, device="cuda")
+        if dense:
+            B.dense_attn(q, k, v, *args, scale, out, lse, ws)
+        else:
+            B.sparse_attn(q, k, v, *args, idx, 0, 2, scale, out, lse, ws)
+        torch.cuda.synchronize()
+        of, lf = to_f64(out), lse.cpu().numpy()
+        n_empty = 0
+        for s in range(2):
+            Ks = R.as_f64(ik.k[kst[s]:kst[s] + klens[s]])
+            Vs = R.as_f64(ik.v[kst[s]:kst[s] + klens[s]])
+            rows_s = range(qlens[s]) if qlens[s] <= 64 else sample_positions(qlens[s], 96, seed=s)
+            edge = {0, qlens[s] - klens[s] - 1, qlens[s] - klens[s]}   # the last row before / first after
+            rows_s = sorted(set(rows_s) | {i for i in edge if 0 <= i < qlens[s]})
+            for i in rows_s:
+                t = klens[s] - qlens[s] + i
+                r = qst[s] + i
+                if t < 0:
+                    n_empty += 1
+                    assert np.all(of[r] == 0.0), (dense, s, i)
+                    assert np.all(np.isneginf(lf[:, r])), (dense, s, i)
+                    continue
+                qv = iq.q[r]
+                if dense:
+                    o_ref, l_ref = R.dense_token(qv, t, Ks, Vs, h_q // h_kv, scale)
+                else:
+                    bt = t // 64
+                    o_ref, l_ref = R.attend_token(qv, t, Ks, Vs, [[b for b in (bt - 1, bt) if b >= 0]] * h_kv,
+                                                  h_q // h_kv, p)
+                ma, rr = attn_errors(of[r], o_ref)
+                assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (dense, s, i, ma, rr)
+                assert np.abs(lf[:, r] - l_ref).max() < 1e-3, (dense, s, i)
+        assert n_empty > 0
+
+
 # ----------------------------------------------------------------------------
 # selection
 # ----------------------------------------------------------------------------
