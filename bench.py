@@ -213,12 +213,13 @@ def main():
                          "kernel of known size, to calibrate HBM byte counters)")
     ap.add_argument("--dense-steps", type=int, default=0,
                     help="also time the dense causal kernel at the same length (context)")
-    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "sweep", "backward", "layer",
-                                           "layer_decode", "unfused"],
+    ap.add_argument("--workload", choices=["prefill", "decode", "varlen", "dense", "sweep", "backward",
+                                           "layer", "layer_decode", "unfused"],
                     default="prefill",
                     help="prefill (default): one 128K sequence; decode: 16 sequences x 128K "
                          "cache, one token each per step; varlen: 65536 packed tokens of mixed "
-                         "lengths through the dense/sparse switch; sweep: the prefill at several "
+                         "lengths through the dense/sparse switch; dense: the switch's short path "
+                         "alone (8 x 8192 packed tokens); sweep: the prefill at several "
                          "selection sizes |I| against the dense kernel at the same length; "
                          "backward: the gradients of the 128K sparse attention (selection "
                          "held fixed); layer: one attention layer of the 8B shape (hidden 4096) "
@@ -240,6 +241,8 @@ def main():
         return bench_decode(args)
     if args.workload == "varlen":
         return bench_varlen(args)
+    if args.workload == "dense":
+        return bench_dense(args)
     if args.workload == "sweep":
         return bench_sweep(args)
     if args.workload == "backward":
@@ -638,6 +641,55 @@ def bench_varlen(args):
         "roofline": {"bound": "mfma", "kernel": "whole step (all kernels)", "achieved": tf,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": tf / PEAK_BF16_TFLOPS,
                      "traffic": None},
+    }
+    print(json.dumps(res), flush=True)
+
+
+def bench_dense(args):
+    """The switch's short path alone: a packed batch of sequences at the
+    dense threshold (8192 tokens each unless --seq is lowered; 65536 tokens
+    in all) through dense causal attention (the library transposes V into
+    its workspace on every call, as the switch does)."""
+    import torch
+
+    from trainable_block_sparse_compress_amd import datagen as D
+    from trainable_block_sparse_compress_amd import pipeline as P
+
+    h_q, h_kv, d = 32, 2, 128
+    cfg = P.SparseConfig()
+    n = min(args.seq, cfg.threshold)
+    lengths = [n] * max(1, 65536 // n)
+    print(f"[bench] dense inputs: {len(lengths)} x {n}", file=sys.stderr, flush=True)
+    inp = D.make_prefill(6, lengths, h_q, h_kv, d)
+    dev = lambda b: torch.from_numpy(b.view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = dev(inp.q), dev(inp.k), dev(inp.v)
+    starts = [i * n for i in range(len(lengths))]
+    plan = P.DensePlan(starts, lengths, starts, lengths, q.shape[0], h_q, h_kv, cfg)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream()
+    for _ in range(args.warmup):
+        plan.run(q, k, v, out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        plan.run(q, k, v, out)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    total = sum(lengths)
+    flops = sum(4.0 * d * h_q * m * (m + 1) / 2 for m in lengths)
+    tf = flops / (ms * 1e-3) / 1e12
+    res = {
+        "metric": f"dense causal prefill tokens/s ({len(lengths)} x {n} packed tokens, 32q/2kv, d128)",
+        "value": total / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic: seeded i.i.d. N(0,1) bf16 Q/K/V",
+        "config": {"workload": f"dense causal attention (the switch's short path), {len(lengths)} "
+                               f"sequences of {n} tokens", "lengths": lengths},
+        "roofline": {"bound": "mfma", "kernel": "infllmv2_dense_attn (V transposition + attn_kernel)",
+                     "achieved": tf, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": tf / PEAK_BF16_TFLOPS, "traffic": None},
     }
     print(json.dumps(res), flush=True)
 
