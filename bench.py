@@ -509,8 +509,11 @@ def run_decode(inp, batch, len0, steps, warmup, lse_mode, graph=True):
         "workload": f"decode, batch {batch}, cache {len0} per sequence, {steps} consecutive "
                     "tokens per sequence",
         "launch": "eager" if g is None else "HIP graph replay of the captured step",
+        "ms_per_step_median": float(np.median(t_step)),
         "ms_select_blocks": float(np.mean(t_sel)) if t_sel else None,
         "ms_sparse_attn": float(np.mean(t_attn)) if t_attn else None,
+        "ms_select_blocks_median": float(np.median(t_sel)) if t_sel else None,
+        "ms_sparse_attn_median": float(np.median(t_attn)) if t_attn else None,
         "roofline": {"bound": "hbm", "kernel": "whole decode step (compress_k + select_blocks + "
                                                 "sparse_attn)",
                      "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
@@ -541,8 +544,10 @@ def bench_decode(args):
         "data": "synthetic: seeded i.i.d. N(0,1) bf16 cache and step tokens, 32 needle blocks/seq",
         "config": {"workload": r["workload"], "h_q": h_q, "h_kv": h_kv, "head_dim": d,
                    "n_init": 1, "n_local": 32, "n_topk": 63, "lse": args.lse},
-        "launch": r["launch"], "ms_select_blocks": r["ms_select_blocks"],
-        "ms_sparse_attn": r["ms_sparse_attn"], "roofline": r["roofline"],
+        "launch": r["launch"], "ms_per_step_median": r["ms_per_step_median"],
+        "ms_select_blocks": r["ms_select_blocks"], "ms_sparse_attn": r["ms_sparse_attn"],
+        "ms_select_blocks_median": r["ms_select_blocks_median"],
+        "ms_sparse_attn_median": r["ms_sparse_attn_median"], "roofline": r["roofline"],
     }
     if cpu is not None:
         res["cpu_baseline"] = cpu
