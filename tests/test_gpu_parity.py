@@ -674,6 +674,50 @@ def test_split_select_short_queries(lib, mode):
                 assert ok, (s, i, g)
 
 
+def test_split_path_many_sequences(lib):
+    """More than 64 sequences on the split-K kernels (one query at the end of
+    each of 80 sequences of 300-6000 keys): the kernels find a row's sequence
+    by binary search instead of the one-round ballot of smaller batches.
+    Selection (exact LSE) and attention over the selected lists are checked
+    against the oracle on a spread of rows, including the first and last
+    sequence."""
+    say("split path, 80 sequences")
+    h_q, h_kv = 32, 2
+    rng = np.random.Generator(np.random.PCG64(81))
+    klens = [int(x) for x in rng.integers(300, 6000, size=80)]
+    qlens = [1] * len(klens)
+    p = R.Params(n_init=1, n_local=4, n_topk=11, lse_mode="exact")
+    pr = p.with_(round_kc=True)
+    inp = D.make_prefill(34, klens, h_q, h_kv, n_needles=2)
+    kst = _starts(klens)
+    qrows = [kst[s] + klens[s] - 1 for s in range(len(klens))]
+    qst = _starts(qlens)
+    plan = P.SparsePlan(qst, qlens, kst, klens, len(qrows), h_q, h_kv, _cfg(p))
+    q = to_dev(np.ascontiguousarray(inp.q[qrows]))
+    k, v = to_dev(inp.k), to_dev(inp.v)
+    out = torch.empty_like(q)
+    plan.run(q, k, v, out)
+    torch.cuda.synchronize()
+    idx = plan.block_idx.cpu().numpy()
+    of = to_f64(out)
+    check = sorted({0, 1, 63, 64, 65, len(klens) - 1} | set(int(x) for x in rng.choice(len(klens), 10, replace=False)))
+    for s in check:
+        t = klens[s] - 1
+        Ks = inp.k[kst[s]:kst[s] + klens[s]]
+        KC1 = R.compress_keys(Ks, 32, 16, True)
+        sel, diag = R.select_token(inp.q[kst[s] + t], t, KC1, None, h_q // h_kv, pr)
+        lists = []
+        for g in range(h_kv):
+            gl = [int(b) for b in idx[g, s] if b >= 0]
+            ok, _, _ = check_selection(gl, sel[g], diag["info"][g], t, pr)
+            assert ok, (s, g)
+            lists.append(gl)
+        o_ref, _ = R.attend_token(inp.q[kst[s] + t], t, R.as_f64(Ks), R.as_f64(inp.v[kst[s]:kst[s] + klens[s]]),
+                                  lists, h_q // h_kv, p)
+        ma, rr = attn_errors(of[s], o_ref)
+        assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (s, ma, rr)
+
+
 def test_end_to_end_extreme_scores(lib):
     """Selection and attention on the extreme-score inputs: the attention
     kernel's running max jumps by up to ~175 log2 units between blocks (its
