@@ -48,6 +48,7 @@ __device__ __forceinline__ u32x4 clip_keys(u32x4 v, int first, int limit) {
 // max exceeds it by more than 8 in log2 units, so P <= 2^8 (exact enough in
 // bf16) and most blocks skip the O rescale.
 constexpr float kLazyLog2 = 8.f;
+constexpr float kLazySum = 256.f;   // 2^kLazyLog2
 
 constexpr int kAttnWaves = 8;                    // waves per workgroup
 constexpr int kTPW = 2;                          // query tokens per wave
@@ -125,53 +126,73 @@ struct Attn {
 
   // Online-softmax update of token k with the S^T tile of block b, then pack
   // P^T as the two B operands (keys 0..31 and 32..63) of the P.V product.
+  // kSumCheck: exponentiate against the running max first, and look for the
+  // block max only when some lane's sum of its 16 values exceeds 2^8.  A sum
+  // bounds each of its terms, so below that no score exceeds the running max
+  // by more than the lazy threshold and the values stand as computed; the
+  // max reduction is skipped on almost every block.  Without it, the block
+  // max is taken first (the multi-window instance, which has no registers to
+  // keep the scores live across the test).  Either way a block raises the
+  // running max only past the threshold, which bounds P and is not a
+  // rounding decision.
+  template <bool kSumCheck>
   __device__ __forceinline__ void softmax_block(int k, int b, const floatx4 (&sacc)[4], bf16x8 (&pb)[2]) {
     float v[4][4];
-    float mx = -__builtin_inff();
     if (b == bt[k]) {          // the query's own block: keys after it are masked
       // key_of(kt, 4*q4 + r) = 8*q4 + (32*(kt/2) + 4*(kt%2) + r): compare the
       // lane-free part against the limit shifted by the lane's 8*q4.
       const int lim = tpos[k] - kBlock * b - 8 * q4;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
+        for (int r = 0; r < 4; ++r)
           v[kt][r] = 32 * (kt >> 1) + 4 * (kt & 1) + r <= lim ? sacc[kt][r] : -__builtin_inff();
-          mx = fmaxf(mx, v[kt][r]);
-        }
-      }
     } else {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[kt][r] = sacc[kt][r];
+    }
+    float p[4][4];
+    float ls = 0.f;
+    const auto exponentiate = [&]() {
+      const float mc = m[k] * a.c;
+      ls = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          v[kt][r] = sacc[kt][r];
-          mx = fmaxf(mx, v[kt][r]);
+          p[kt][r] = fast_exp2(fmaf(v[kt][r], a.c, -mc));
+          ls += p[kt][r];
         }
-      }
-    }
-    mx = max_x32(max_x16(mx));
-    if (__ballot(mx * a.c > m[k] * a.c + kLazyLog2) != 0) {
+    };
+    // Raise the running max to the block max (rescaling l and O) when the
+    // block max exceeds it by more than the lazy threshold; true if raised.
+    const auto raise_max = [&]() -> bool {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, v[kt][r]);
+      mx = max_x32(max_x16(mx));
+      if (__ballot(mx * a.c > m[k] * a.c + kLazyLog2) == 0) return false;
       const float mn = fmaxf(m[k], mx);
       const float alpha = fast_exp2((m[k] - mn) * a.c);
       m[k] = mn;
       l[k] *= alpha;
 #pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
+      for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
         for (int r = 0; r < 4; ++r) o[k][dt][r] *= alpha;
-      }
-    }
-    const float mc = m[k] * a.c;
-    float p[4][4];
-    float ls = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        p[kt][r] = fast_exp2(fmaf(v[kt][r], a.c, -mc));
-        ls += p[kt][r];
-      }
+      return true;
+    };
+    if constexpr (kSumCheck) {
+      exponentiate();
+      // (an infinite or NaN sum, as on a token's first block, fails <=)
+      if (__ballot(!(ls <= kLazySum)) != 0 && raise_max()) exponentiate();
+    } else {
+      raise_max();
+      exponentiate();
     }
     l[k] += ls;
 #pragma unroll
@@ -297,6 +318,7 @@ struct Attn {
 
   // Shared phase: block b (staged in lk / lv) for the tokens of this wave
   // whose bit is set in sel.  The V^T loads are in flight during the softmax.
+  template <bool kSumCheck>
   __device__ __forceinline__ void consume(uint32_t sel, const uint8_t* lk, const uint8_t* lv, int b) {
     floatx4 sacc[kTPW][4];
     // MFMA stretches run at raised wave priority, so the other wave on the
@@ -312,7 +334,7 @@ struct Attn {
     bf16x8 pb[kTPW][2];
 #pragma unroll
     for (int k = 0; k < kTPW; ++k)
-      if ((sel >> k) & 1u) softmax_block(k, b, sacc[k], pb[k]);
+      if ((sel >> k) & 1u) softmax_block<kSumCheck>(k, b, sacc[k], pb[k]);
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int k = 0; k < kTPW; ++k) {
@@ -352,6 +374,7 @@ struct Attn {
 
   // Private phase, block b for the tokens of this wave in sel: K from the
   // wave's region, V^T from registers (keys past the sequence zeroed).
+  template <bool kSumCheck>
   __device__ __forceinline__ void consume_private(uint32_t sel, const uint8_t* lk, u32x4 (&vb)[8][2], int b) {
     if (kBlock * b + kBlock > rk.len) {
 #pragma unroll
@@ -377,7 +400,7 @@ struct Attn {
       }
       __builtin_amdgcn_s_setprio(0);
       bf16x8 pb[2];
-      softmax_block(k, b, sacc, pb);
+      softmax_block<kSumCheck>(k, b, sacc, pb);
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
@@ -554,10 +577,10 @@ struct Attn {
         if (u + 2 < n_ent) stage_issue(sh.ring[2 * (half ^ 1)][0], sh.ring[2 * (half ^ 1)][1], sh.ub[u + 2]);
         if (u + 3 < n_ent) stage_issue(sh.ring[2 * (half ^ 1) + 1][0], sh.ring[2 * (half ^ 1) + 1][1], sh.ub[u + 3]);
         const uint32_t m0 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u]));
-        if (m0) consume(m0, sh.ring[2 * half][0], sh.ring[2 * half][1], b0);
+        if (m0) consume<kSingle>(m0, sh.ring[2 * half][0], sh.ring[2 * half][1], b0);
         if (b1 >= 0) {
           const uint32_t m1 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u + 1]));
-          if (m1) consume(m1, sh.ring[2 * half + 1][0], sh.ring[2 * half + 1][1], b1);
+          if (m1) consume<kSingle>(m1, sh.ring[2 * half + 1][0], sh.ring[2 * half + 1][1], b1);
         }
       }
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -596,7 +619,7 @@ struct Attn {
         uint32_t sn = 0;
         const int bn = next_block(sn);
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // K(bc) in the region, V(bc) in registers
-        consume_private(sc, region, vb, bc);
+        consume_private<kSingle>(sc, region, vb, bc);
         if (bn >= 0) {
           __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): the region's K reads are done
           issue_k_private(region, bn);
@@ -866,36 +889,50 @@ __global__ __launch_bounds__(kSplitThreads, 2) void attn_split_kernel(AttnArgs a
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) sacc[kt] = mfma16(kf[kt][ks], qb[ks], sacc[kt]);
     }
-    // Online softmax update (keys after the query masked in its own block).
-    float v[4][4], mx = -__builtin_inff();
+    // Online softmax update (keys after the query masked in its own block),
+    // exponentiated against the running max first; the block max is looked
+    // for only when some lane's sum passes 2^8 (see the tile kernel).
+    float v[4][4];
     const int lim = t - kBlock * b - 8 * q4;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
+      for (int rr = 0; rr < 4; ++rr)
         v[kt][rr] = (b < bt || 32 * (kt >> 1) + 4 * (kt & 1) + rr <= lim) ? sacc[kt][rr] : -__builtin_inff();
-        mx = fmaxf(mx, v[kt][rr]);
-      }
-    mx = max_x32(max_x16(mx));
-    if (__ballot(mx * a.c > m * a.c + kLazyLog2) != 0) {
-      const float mn = fmaxf(m, mx);
-      const float alpha = fast_exp2((m - mn) * a.c);
-      m = mn;
-      l *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) o[dt][rr] *= alpha;
-    }
-    const float mc = m * a.c;
     float p[4][4];
+    float ls = 0.f;
+    const auto exponentiate = [&]() {
+      const float mc = m * a.c;
+      ls = 0.f;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
+      for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        p[kt][rr] = fast_exp2(fmaf(v[kt][rr], a.c, -mc));
-        l += p[kt][rr];
+        for (int rr = 0; rr < 4; ++rr) {
+          p[kt][rr] = fast_exp2(fmaf(v[kt][rr], a.c, -mc));
+          ls += p[kt][rr];
+        }
+    };
+    exponentiate();
+    if (__ballot(!(ls <= kLazySum)) != 0) {
+      float mx = -__builtin_inff();
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) mx = fmaxf(mx, v[kt][rr]);
+      mx = max_x32(max_x16(mx));
+      if (__ballot(mx * a.c > m * a.c + kLazyLog2) != 0) {
+        const float mn = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - mn) * a.c);
+        m = mn;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr) o[dt][rr] *= alpha;
+        exponentiate();
       }
+    }
+    l += ls;
     bf16x8 pb[2];
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
