@@ -209,7 +209,9 @@ int infllmv2_select_blocks_unfused(const void* q, const void* k_c1, const void* 
  *              the library transposes it into the workspace once per call);
  *              v_seq_stride  > 0: bf16 [h_kv, head_dim, batch, v_seq_stride]
  *              (a transposed cache: sequence s's key i at column i; the stride
- *              must be a multiple of 64; columns past len_k(s) are never used)
+ *              must be a multiple of 64; columns past len_k(s) are never used).
+ *              batch x columns (v_seq_stride, or max_seqlen_k rounded up to 64)
+ *              must stay below 2^27, else INFLLMV2_EUNSUPPORTED.
  *   block_idx  int32 [h_kv, rows_q, n_sel]
  *   lse_out    float [h_q, rows_q] natural-log softmax normaliser, or NULL
  *   workspace  size from a query with the same shape arguments: the

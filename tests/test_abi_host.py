@@ -138,6 +138,13 @@ def test_attention_validation_and_workspace(lib):
                                   32, 2, 128, 32, None, 96, 1, 32, 0.088, 0, None, None, None,
                                   ctypes.byref(size), None)
     assert rc == EUNSUP  # block size 32
+    # transposed-V rows of batch x columns at the 2^27 limit (the kernel's
+    # 32-bit offsets over 16 such rows) are refused; one column less is not
+    for stride, code in ((1 << 20, EUNSUP), ((1 << 20) - 64, OK)):
+        rc = lib.infllmv2_sparse_attn(None, None, None, None, None, None, None, 128, 1, 64, 128, 0,
+                                      32, 2, 128, 64, None, 96, 1, 32, 0.088, stride, None, None,
+                                      None, ctypes.byref(size), None)
+        assert rc == code, (stride, rc)
 
 
 def test_compress_validation(lib):

@@ -51,6 +51,9 @@ bool group_ok(int G) { return G == 1 || G == 2 || G == 4 || G == 8 || G == 16; }
 
 constexpr int kMaxBlocks = 8192;      // per sequence (top-k keeps <= 128 keys per lane)
 constexpr int kMaxGrid = 65535;
+// batch x columns of one transposed-V row: 16 such rows of bf16 stay under
+// 4 GiB, the reach of the attention kernel's 32-bit offsets.
+constexpr int64_t kMaxVtRow = (int64_t)1 << 27;
 
 // Workspace of the scoring path: fp32 LSE [h_q, rows_q] + fp32 block scores
 // [h_kv, rows_q, bs_ld].
@@ -209,6 +212,12 @@ int attn_common(const void* q, const void* k, const void* v, const int32_t* cu_s
     REQUIRE(v_seq_stride >= round_up(max_seqlen_k, kBlock), INFLLMV2_EINVAL,
             "v_seq_stride %lld < max_seqlen_k rounded to 64", (long long)v_seq_stride);
   }
+  // The tile kernel addresses 16 rows of the transposed V (head-dim rows of
+  // batch x columns each) with 32-bit offsets from one base.
+  const int64_t vt_cols = v_seq_stride > 0 ? v_seq_stride : round_up(std::max(1, max_seqlen_k), kBlock);
+  REQUIRE((int64_t)batch * vt_cols < kMaxVtRow, INFLLMV2_EUNSUPPORTED,
+          "batch x transposed-V columns %lld reaches the limit of %lld",
+          (long long)((int64_t)batch * vt_cols), (long long)kMaxVtRow);
   const int splits = attn_splits(rows_q, batch, max_seqlen_q, max_seqlen_k, h_kv, dense, n_sel,
                                  n_init, n_local);
   const size_t vt_need = v_seq_stride > 0 ? 0 : vt_bytes(h_kv, batch, max_seqlen_k);

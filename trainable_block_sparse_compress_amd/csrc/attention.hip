@@ -206,15 +206,30 @@ struct Attn {
     }
   }
 
-  // Global addressing of K and V^T blocks: a uniform base per block plus
-  // lane-constant offsets (set once by init_offsets).
-  const uint16_t* kbase;   // K row 0 of this sequence, this KV group
-  const uint16_t* vbase;   // V^T dim 0 of this sequence, this KV group
-  int64_t krow;            // elements between consecutive K rows
-  int64_t vdim;            // elements between consecutive V^T dims
-  int klo[2];              // K staging: lane offset in a 4-row part, per swizzle variant
-  int64_t vlo_stage;       // V^T staging: lane offset in an 8-dim part
-  int64_t vlo_frag;        // V^T fragment loads: lane offset (dim c16, keys 8*q4)
+  // Global addressing of K and V^T blocks: buffer loads from a wave-uniform
+  // base (a buffer descriptor in scalar registers, rebuilt per block) plus a
+  // uniform offset and a 32-bit lane byte offset set once by init_offsets,
+  // so no load costs per-lane 64-bit address arithmetic.
+  const char* kbase;       // K row 0 of this sequence, this KV group
+  const char* vbase;       // V^T dim 0 of this sequence, this KV group
+  int64_t krow;            // bytes between consecutive K rows
+  int64_t vdim;            // bytes between consecutive V^T dims
+  uint32_t klo[2];         // K staging: lane byte offset in a 4-row part, per swizzle variant
+  uint32_t vlo_stage;      // V^T staging: lane byte offset in an 8-dim part
+  uint32_t vlo_frag;       // V^T fragment loads: lane byte offset (dim c16, keys 8*q4)
+  static __device__ __forceinline__ int64_t uniform64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+  }
+  // Raw buffer over [base, base + 4 GiB): stride 0, no record limit, the
+  // gfx9-family word 3 (32-bit data format).
+  static __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const char* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, -1, 0x00020000);
+  }
+  static __device__ __forceinline__ void buf_lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint8_t* dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
+  }
 
   // K row `row` (relative to the sequence), chunk ch, clamped to the tensor.
   __device__ __forceinline__ const uint16_t* k_clamped(int row, int ch) const {
@@ -243,24 +258,20 @@ struct Attn {
   // fix_partial().
   __device__ __forceinline__ void stage_issue(uint8_t* lk, uint8_t* lv, int b) const {
     if (k_inside(b)) {
-      const int lo0 = opaque(klo[0]), lo1 = opaque(klo[1]);
-      const uint16_t* base = kbase + (int64_t)(kBlock * b) * krow;
+      const auto r = rsrc(kbase + (int64_t)(kBlock * b) * krow);
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
         const int part = wave + kAttnWaves * j;
-        __builtin_amdgcn_global_load_lds(base + (int64_t)(4 * part) * krow + ((part & 2) ? lo1 : lo0),
-                                         (__attribute__((address_space(3))) void*)(lk + part * 1024), 16, 0, 0);
+        buf_lds16(r, (part & 2) ? klo[1] : klo[0], (uint32_t)((4 * part) * krow), lk + part * 1024);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) stage_k_part(lk, b, wave + kAttnWaves * j);
     }
-    const uint16_t* pv = vbase + (int64_t)kBlock * b + opaque64(vlo_stage);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int part = wave + kAttnWaves * j;   // dims 8*part .. 8*part+7
-      __builtin_amdgcn_global_load_lds(pv + (int64_t)(8 * part) * vdim,
-                                       (__attribute__((address_space(3))) void*)(lv + part * 1024), 16, 0, 0);
+      buf_lds16(rsrc(vbase + (int64_t)(2 * kBlock) * b + (int64_t)(8 * part) * vdim), vlo_stage, 0u, lv + part * 1024);
     }
   }
   // Zero the V^T columns of keys >= len_k in a staged partial block.
@@ -279,15 +290,18 @@ struct Attn {
   // V^T fragment (dt, kk) at voff[kk] + 2048*dt.
   int koff[4], voff[2];
   __device__ __forceinline__ void init_offsets() {
-    krow = (int64_t)a.h_kv * kHeadDim;
-    vdim = (int64_t)a.batch * a.vt_ld;
-    kbase = a.k + ((int64_t)rk.start * a.h_kv + g) * kHeadDim;
-    vbase = a.vt + ((int64_t)g * kHeadDim * a.batch + s) * a.vt_ld;
+    krow = uniform64((int64_t)a.h_kv * kHeadDim * 2);
+    vdim = uniform64((int64_t)a.batch * a.vt_ld * 2);
+    kbase = reinterpret_cast<const char*>(
+        uniform64(reinterpret_cast<int64_t>(a.k + ((int64_t)rk.start * a.h_kv + g) * kHeadDim)));
+    vbase = reinterpret_cast<const char*>(
+        uniform64(reinterpret_cast<int64_t>(a.vt + ((int64_t)g * kHeadDim * a.batch + s) * a.vt_ld)));
+    // (the host keeps 16 V^T dims under 4 GiB, so every offset fits 32 bits)
 #pragma unroll
     for (int v = 0; v < 2; ++v)
-      klo[v] = (lane >> 4) * (int)krow + 8 * ((lane & 15) ^ (((lane >> 4) & 3) | (4 * v)));
-    vlo_stage = (int64_t)(lane >> 3) * vdim + 8 * ((lane & 7) ^ ((lane >> 3) & 7));
-    vlo_frag = (int64_t)c16 * vdim + 8 * q4;
+      klo[v] = (uint32_t)((lane >> 4) * krow + 16 * ((lane & 15) ^ (((lane >> 4) & 3) | (4 * v))));
+    vlo_stage = (uint32_t)((lane >> 3) * vdim + 16 * ((lane & 7) ^ ((lane >> 3) & 7)));
+    vlo_frag = (uint32_t)(c16 * vdim + 16 * q4);
     const int key0 = 8 * (c16 >> 2) + (c16 & 3);
     const int sw = swz_k(key0);   // equal for every key of this lane
 #pragma unroll
@@ -351,12 +365,10 @@ struct Attn {
   // (16 direct global->LDS loads of 1 KB, same swizzled layout as the ring).
   __device__ __forceinline__ void issue_k_private(uint8_t* lk, int b) const {
     if (k_inside(b)) {
-      const int lo0 = opaque(klo[0]), lo1 = opaque(klo[1]);
-      const uint16_t* base = kbase + (int64_t)(kBlock * b) * krow;
+      const auto r = rsrc(kbase + (int64_t)(kBlock * b) * krow);
 #pragma unroll
       for (int part = 0; part < 16; ++part)
-        __builtin_amdgcn_global_load_lds(base + (int64_t)(4 * part) * krow + ((part & 2) ? lo1 : lo0),
-                                         (__attribute__((address_space(3))) void*)(lk + part * 1024), 16, 0, 0);
+        buf_lds16(r, (part & 2) ? klo[1] : klo[0], (uint32_t)((4 * part) * krow), lk + part * 1024);
     } else {
 #pragma unroll
       for (int part = 0; part < 16; ++part) stage_k_part(lk, b, part);
@@ -365,11 +377,12 @@ struct Attn {
   // Private phase: V^T fragments of block b straight into registers
   // (fragment (dt, kk): dim 16*dt + c16, keys 64*b + 32*kk + 8*q4 .. +8).
   __device__ __forceinline__ void load_v_private(u32x4 (&vb)[8][2], int b) const {
-    const uint16_t* p = vbase + (int64_t)kBlock * b + opaque64(vlo_frag);
 #pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
+    for (int dt = 0; dt < 8; ++dt) {
+      const auto r = rsrc(vbase + (int64_t)(2 * kBlock) * b + (int64_t)(16 * dt) * vdim);
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) vb[dt][kk] = ldg16(p + (int64_t)(16 * dt) * vdim + 32 * kk);
+      for (int kk = 0; kk < 2; ++kk) vb[dt][kk] = __builtin_amdgcn_raw_buffer_load_b128(r, vlo_frag + 64 * kk, 0, 0);
+    }
   }
 
   // Private phase, block b for the tokens of this wave in sel: K from the
