@@ -4,8 +4,9 @@
 // and the sliding window are one sparse attention, with the local blocks
 // extended to cover the window (top168.com article on InfLLM-V2, section 七
 // "技术实现的创新细节"; reading notes "论文阅读：InfLLM-V2", section "对齐计算图").
-// The dense path below the length threshold is the same kernel with every
-// causal block treated as shared.
+// The dense path below the length threshold is an instance of the same
+// kernel in which every causal block is shared and the block list and token
+// masks follow by arithmetic.
 //
 // Per workgroup: 16 consecutive query tokens of one sequence and one KV group,
 // 8 waves of 2 tokens.  Every block the tokens attend is listed once with a
@@ -428,143 +429,157 @@ struct Attn {
   // single-window kernel, which also balances the tokens over the waves and
   // orders the shared list (both left out of the multi-window kernel, whose
   // loop keeps every token on its wave and leaves no registers to spare).
-  template <bool kSingle>
-  __device__ __forceinline__ void window(AttnLds& sh, int w0, int w1, int nq, int pos0, int i0,
-                                         bool dense, int tid) {
-    // 1. init / local (dense: every causal block), by arithmetic.
-    if (tid < kTileTok) sh.pcnt[tid] = 0;
-    for (int b = w0 + tid; b < w1; b += kThreads) {
-      uint32_t msk = 0;
-      // (a block past the V^T row would mean inconsistent lengths: skipped)
-      for (int tk = 0; tk < nq && kBlock * b + kBlock <= a.vt_ld; ++tk) {
-        const int t = pos0 + i0 + tk;
-        if (t < 0 || (int64_t)rq.start + i0 + tk >= a.rows_q) continue;
-        const int btk = t / kBlock;
-        const bool rel = b <= btk && (dense || b < a.n_init || b >= btk - a.n_local + 1);
-        msk |= (uint32_t)rel << tk;
-      }
-      sh.mask[b - w0] = msk;
-    }
-    __syncthreads();
-    // 2. top-k entries of the tile's tokens (set union; -1, repeats and
-    //    blocks after the token's own are ignored).
-    if (!dense) {
-#pragma unroll
-      for (int k = 0; k < kTPW; ++k) {
-        if (!tval[k]) continue;
-        const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + trow[k]) * a.n_sel;
-        const uint32_t bit = 1u << tb[k];
-        for (int e = lane; e < a.n_sel; e += 64) {
-          const int b = list[e];
-          if (b >= 0 && b <= bt[k] && b >= w0 && b < w1 && kBlock * b + kBlock <= a.vt_ld)
-            atomicOr(&sh.mask[b - w0], bit);
-        }
-      }
-    }
-    __syncthreads();
-    // 3. compact the shared-phase blocks, ascending: entry e = 512*j + tid
-    //    goes to (blocks before round j) + (blocks of earlier waves in
-    //    round j) + (earlier lanes of this wave).
+  template <bool kSingle, bool kDense>
+  __device__ __forceinline__ void window(AttnLds& sh, int w0, int w1, int nq, int pos0, int i0, int tid) {
+    constexpr bool dense = kDense;
     const int nblk = w1 - w0;
-    uint64_t bal[kWin / kThreads];
-#pragma unroll
-    for (int j = 0; j < kWin / kThreads; ++j) {
-      const int e = kThreads * j + tid;
-      const uint32_t v = e < nblk ? sh.mask[e] : 0u;
-      bal[j] = __ballot(v != 0u && (dense || __builtin_popcount(v) >= kShareMin));
-      if (kSingle && !dense && v != 0u && __builtin_popcount(v) < kShareMin) {
-        for (uint32_t x = v; x != 0u; x &= x - 1u) atomicAdd(&sh.pcnt[__builtin_ctz(x)], 1);
-      }
-      if (lane == 0) sh.cnt[j][wave] = __builtin_popcountll(bal[j]);
-    }
-    __syncthreads();
     int n_ent = 0;
-#pragma unroll
-    for (int j = 0; j < kWin / kThreads; ++j) {
-      int before = 0, total = 0;
-#pragma unroll
-      for (int w = 0; w < kAttnWaves; ++w) {
-        const int c = sh.cnt[j][w];
-        before += w < wave ? c : 0;
-        total += c;
+    // Dense: tile tokens [dlo, dhi) are valid (position >= 0, row inside
+    // the tensor), and the shared list is every block of the window up to
+    // the last valid token's own (none past the V^T row), entry u being
+    // block w0 + u with its token mask by arithmetic (ent_mask below).
+    const int p0 = pos0 + i0;
+    const int dlo = max(0, -p0);
+    const int dhi = (int)min<int64_t>(nq, a.rows_q - rq.start - i0);
+    if constexpr (dense) {
+      if (dlo < dhi) {
+        const int last = min(min(w1, (p0 + dhi - 1) / kBlock + 1), (int)(a.vt_ld / kBlock));
+        n_ent = max(0, last - w0);
       }
-      if ((bal[j] >> lane) & 1ull) {
-        const int e = kThreads * j + tid;
-        const int pos = n_ent + before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
-                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
-        sh.ub[pos] = w0 + e;
-        sh.um[pos] = sh.mask[e];
-      }
-      n_ent += total;
-    }
-    __syncthreads();
-    // 3a. balance the private phase: the tokens ranked by private block
-    //     count are paired heaviest with lightest, one pair per wave, and the
-    //     waves take over their new tokens (no token has been touched yet).
-    if (kSingle && !dense) {
-      static_assert(kTPW == 2, "the pairing gives each wave two tokens");
-      if (wave == 0 && lane < kTileTok) {
-        const int c = sh.pcnt[lane];
-        int rank = 0;
-#pragma unroll
-        for (int j = 0; j < kTileTok; ++j) {
-          const int cj = sh.pcnt[j];
-          rank += (cj > c || (cj == c && j < lane)) ? 1 : 0;
+    } else {
+      // 1. init / local, by arithmetic.
+      if (tid < kTileTok) sh.pcnt[tid] = 0;
+      for (int b = w0 + tid; b < w1; b += kThreads) {
+        uint32_t msk = 0;
+        // (a block past the V^T row would mean inconsistent lengths: skipped)
+        for (int tk = 0; tk < nq && kBlock * b + kBlock <= a.vt_ld; ++tk) {
+          const int t = pos0 + i0 + tk;
+          if (t < 0 || (int64_t)rq.start + i0 + tk >= a.rows_q) continue;
+          const int btk = t / kBlock;
+          const bool rel = b <= btk && (b < a.n_init || b >= btk - a.n_local + 1);
+          msk |= (uint32_t)rel << tk;
         }
-        const int slot = rank < kTileTok / 2 ? kTPW * rank : kTPW * (kTileTok - 1 - rank) + 1;
-        sh.perm[slot] = lane;
+        sh.mask[b - w0] = msk;
       }
       __syncthreads();
+      // 2. top-k entries of the tile's tokens (set union; -1, repeats and
+      //    blocks after the token's own are ignored).
+      {
 #pragma unroll
-      for (int k = 0; k < kTPW; ++k) {
-        const int tt = __builtin_amdgcn_readfirstlane(sh.perm[wave * kTPW + k]);
-        if (tt != tb[k]) init_token(k, tt, i0, pos0);
-      }
-    }
-    // 3b. order the shared list for balance: within each run of 64 entries an
-    //     entry is followed by the first later one whose tokens lie in other
-    //     waves (else by the next one), so the two blocks of a batch tend to
-    //     occupy different waves.  Runs are 64 entries, so batches of two
-    //     never straddle them.
-    if (kSingle && !dense) {
-      for (int c = wave; 64 * c < n_ent; c += kAttnWaves) {
-        const int cnt = min(64, n_ent - 64 * c);
-        const bool ok = lane < cnt;
-        const int32_t ubv = ok ? sh.ub[64 * c + lane] : 0;
-        const uint32_t umv = ok ? sh.um[64 * c + lane] : 0u;
-        uint32_t wm = 0;
-#pragma unroll
-        for (int w = 0; w < kAttnWaves; ++w) {
-          uint32_t wb = 0;
-#pragma unroll
-          for (int k = 0; k < kTPW; ++k) wb |= 1u << sh.perm[kTPW * w + k];
-          wm |= (uint32_t)((umv & wb) != 0u) << w;
-        }
-        const uint64_t valid = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
-        uint64_t used = 0;
-        int dest = 0, p = 0;
-        for (int i = 0; i < cnt; ++i) {
-          if ((used >> i) & 1ull) continue;
-          used |= 1ull << i;
-          dest = lane == i ? p : dest;
-          ++p;
-          const uint32_t aw = __builtin_amdgcn_readlane(wm, i);
-          const uint64_t later = valid & ~used & ~((2ull << i) - 1ull);
-          uint64_t cand = __ballot((wm & aw) == 0u) & later;
-          if (cand == 0) cand = later;
-          if (cand != 0) {
-            const int j = (int)__builtin_ctzll(cand);
-            used |= 1ull << j;
-            dest = lane == j ? p : dest;
-            ++p;
+        for (int k = 0; k < kTPW; ++k) {
+          if (!tval[k]) continue;
+          const int32_t* list = a.bidx + ((int64_t)g * a.rows_q + trow[k]) * a.n_sel;
+          const uint32_t bit = 1u << tb[k];
+          for (int e = lane; e < a.n_sel; e += 64) {
+            const int b = list[e];
+            if (b >= 0 && b <= bt[k] && b >= w0 && b < w1 && kBlock * b + kBlock <= a.vt_ld)
+              atomicOr(&sh.mask[b - w0], bit);
           }
         }
-        if (ok) {
-          sh.ub[64 * c + dest] = ubv;
-          sh.um[64 * c + dest] = umv;
-        }
       }
       __syncthreads();
+      // 3. compact the shared-phase blocks, ascending: entry e = 512*j + tid
+      //    goes to (blocks before round j) + (blocks of earlier waves in
+      //    round j) + (earlier lanes of this wave).
+      uint64_t bal[kWin / kThreads];
+#pragma unroll
+      for (int j = 0; j < kWin / kThreads; ++j) {
+        const int e = kThreads * j + tid;
+        const uint32_t v = e < nblk ? sh.mask[e] : 0u;
+        bal[j] = __ballot(v != 0u && __builtin_popcount(v) >= kShareMin);
+        if (kSingle && v != 0u && __builtin_popcount(v) < kShareMin) {
+          for (uint32_t x = v; x != 0u; x &= x - 1u) atomicAdd(&sh.pcnt[__builtin_ctz(x)], 1);
+        }
+        if (lane == 0) sh.cnt[j][wave] = __builtin_popcountll(bal[j]);
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < kWin / kThreads; ++j) {
+        int before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kAttnWaves; ++w) {
+          const int c = sh.cnt[j][w];
+          before += w < wave ? c : 0;
+          total += c;
+        }
+        if ((bal[j] >> lane) & 1ull) {
+          const int e = kThreads * j + tid;
+          const int pos = n_ent + before + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal[j] >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal[j], 0u));
+          sh.ub[pos] = w0 + e;
+          sh.um[pos] = sh.mask[e];
+        }
+        n_ent += total;
+      }
+      __syncthreads();
+      // 3a. balance the private phase: the tokens ranked by private block
+      //     count are paired heaviest with lightest, one pair per wave, and the
+      //     waves take over their new tokens (no token has been touched yet).
+      if (kSingle) {
+        static_assert(kTPW == 2, "the pairing gives each wave two tokens");
+        if (wave == 0 && lane < kTileTok) {
+          const int c = sh.pcnt[lane];
+          int rank = 0;
+#pragma unroll
+          for (int j = 0; j < kTileTok; ++j) {
+            const int cj = sh.pcnt[j];
+            rank += (cj > c || (cj == c && j < lane)) ? 1 : 0;
+          }
+          const int slot = rank < kTileTok / 2 ? kTPW * rank : kTPW * (kTileTok - 1 - rank) + 1;
+          sh.perm[slot] = lane;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < kTPW; ++k) {
+          const int tt = __builtin_amdgcn_readfirstlane(sh.perm[wave * kTPW + k]);
+          if (tt != tb[k]) init_token(k, tt, i0, pos0);
+        }
+      }
+      // 3b. order the shared list for balance: within each run of 64 entries an
+      //     entry is followed by the first later one whose tokens lie in other
+      //     waves (else by the next one), so the two blocks of a batch tend to
+      //     occupy different waves.  Runs are 64 entries, so batches of two
+      //     never straddle them.
+      if (kSingle) {
+        for (int c = wave; 64 * c < n_ent; c += kAttnWaves) {
+          const int cnt = min(64, n_ent - 64 * c);
+          const bool ok = lane < cnt;
+          const int32_t ubv = ok ? sh.ub[64 * c + lane] : 0;
+          const uint32_t umv = ok ? sh.um[64 * c + lane] : 0u;
+          uint32_t wm = 0;
+#pragma unroll
+          for (int w = 0; w < kAttnWaves; ++w) {
+            uint32_t wb = 0;
+#pragma unroll
+            for (int k = 0; k < kTPW; ++k) wb |= 1u << sh.perm[kTPW * w + k];
+            wm |= (uint32_t)((umv & wb) != 0u) << w;
+          }
+          const uint64_t valid = cnt == 64 ? ~0ull : ((1ull << cnt) - 1ull);
+          uint64_t used = 0;
+          int dest = 0, p = 0;
+          for (int i = 0; i < cnt; ++i) {
+            if ((used >> i) & 1ull) continue;
+            used |= 1ull << i;
+            dest = lane == i ? p : dest;
+            ++p;
+            const uint32_t aw = __builtin_amdgcn_readlane(wm, i);
+            const uint64_t later = valid & ~used & ~((2ull << i) - 1ull);
+            uint64_t cand = __ballot((wm & aw) == 0u) & later;
+            if (cand == 0) cand = later;
+            if (cand != 0) {
+              const int j = (int)__builtin_ctzll(cand);
+              used |= 1ull << j;
+              dest = lane == j ? p : dest;
+              ++p;
+            }
+          }
+          if (ok) {
+            sh.ub[64 * c + dest] = ubv;
+            sh.um[64 * c + dest] = umv;
+          }
+        }
+        __syncthreads();
+      }
     }
     // 4. shared phase: walk the list; the next batch's staging loads are in
     //    flight while the current one computes.
@@ -572,14 +587,23 @@ struct Attn {
       // Batches of two blocks: the ring holds the batch being consumed and
       // the next one in flight; one barrier per batch, so the per-wave load
       // imbalance of single blocks averages over two.
-      stage_issue(sh.ring[0][0], sh.ring[0][1], sh.ub[0]);
-      if (n_ent > 1) stage_issue(sh.ring[1][0], sh.ring[1][1], sh.ub[1]);
+      // Entry u of the list: its block and the tile tokens attending it.
+      const auto ent_block = [&](int u) -> int {
+        return dense ? w0 + u : __builtin_amdgcn_readfirstlane(sh.ub[u]);
+      };
+      const auto ent_mask = [&](int u, int b) -> uint32_t {
+        if (!dense) return __builtin_amdgcn_readfirstlane(sh.um[u]);
+        const int lo = max(dlo, kBlock * b - p0);   // tokens at positions >= 64 b
+        return lo < dhi ? ((1u << dhi) - 1u) & ~((1u << lo) - 1u) : 0u;
+      };
+      stage_issue(sh.ring[0][0], sh.ring[0][1], ent_block(0));
+      if (n_ent > 1) stage_issue(sh.ring[1][0], sh.ring[1][1], ent_block(1));
       for (int u = 0; u < n_ent; u += 2) {
         const int half = (u >> 1) & 1;
         __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // this wave's part of the batch has landed
         __syncthreads();                            // ... every wave's; the other half is free
-        const int b0 = __builtin_amdgcn_readfirstlane(sh.ub[u]);
-        const int b1 = u + 1 < n_ent ? __builtin_amdgcn_readfirstlane(sh.ub[u + 1]) : -1;
+        const int b0 = ent_block(u);
+        const int b1 = u + 1 < n_ent ? ent_block(u + 1) : -1;
         const bool p0 = kBlock * b0 + kBlock > rk.len;
         const bool p1 = b1 >= 0 && kBlock * b1 + kBlock > rk.len;
         if (p0 || p1) {
@@ -587,12 +611,12 @@ struct Attn {
           if (p1) fix_partial(sh.ring[2 * half + 1][1], b1);
           __syncthreads();
         }
-        if (u + 2 < n_ent) stage_issue(sh.ring[2 * (half ^ 1)][0], sh.ring[2 * (half ^ 1)][1], sh.ub[u + 2]);
-        if (u + 3 < n_ent) stage_issue(sh.ring[2 * (half ^ 1) + 1][0], sh.ring[2 * (half ^ 1) + 1][1], sh.ub[u + 3]);
-        const uint32_t m0 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u]));
+        if (u + 2 < n_ent) stage_issue(sh.ring[2 * (half ^ 1)][0], sh.ring[2 * (half ^ 1)][1], ent_block(u + 2));
+        if (u + 3 < n_ent) stage_issue(sh.ring[2 * (half ^ 1) + 1][0], sh.ring[2 * (half ^ 1) + 1][1], ent_block(u + 3));
+        const uint32_t m0 = sel_of(ent_mask(u, b0));
         if (m0) consume<kSingle>(m0, sh.ring[2 * half][0], sh.ring[2 * half][1], b0);
         if (b1 >= 0) {
-          const uint32_t m1 = sel_of(__builtin_amdgcn_readfirstlane(sh.um[u + 1]));
+          const uint32_t m1 = sel_of(ent_mask(u + 1, b1));
           if (m1) consume<kSingle>(m1, sh.ring[2 * half + 1][0], sh.ring[2 * half + 1][1], b1);
         }
       }
@@ -644,7 +668,7 @@ struct Attn {
     }
   }
 
-  template <bool kMulti>
+  template <bool kMulti, bool kDense>
   __device__ void run(AttnLds& sh) {
     // XCD-aware order: workgroups are dispatched round-robin over the 8
     // XCDs; remap them so each XCD walks a contiguous range of query tiles
@@ -653,7 +677,7 @@ struct Attn {
     const unsigned N = nx * ny * gridDim.z;
     const unsigned L = blockIdx.x + nx * (blockIdx.y + ny * blockIdx.z);
     unsigned T;
-    if (a.bidx == nullptr && 8u * nx > N) {
+    if (kDense && 8u * nx > N) {
       // Dense causal over a sequence longer than one XCD's share of the
       // grid: a tile's work grows with its position, and contiguous ranges
       // left the XCDs holding the last tiles with most of the work (measured
@@ -689,7 +713,6 @@ struct Attn {
     lane = tid & 63;
     q4 = lane >> 4;
     c16 = lane & 15;
-    const bool dense = a.bidx == nullptr;
     init_offsets();
 
 #pragma unroll
@@ -702,10 +725,10 @@ struct Attn {
     // both phases' address registers live at once).  Blocks past the V^T row
     // are never attended, so clamping to kWin there loses nothing.
     if constexpr (!kMulti) {
-      window<true>(sh, 0, min(bt_last + 1, kWin), nq, pos0, i0, dense, tid);
+      window<true, kDense>(sh, 0, min(bt_last + 1, kWin), nq, pos0, i0, tid);
     } else {
       for (int w0 = 0; w0 <= bt_last; w0 += kWin) {
-        window<false>(sh, w0, min(bt_last + 1, w0 + kWin), nq, pos0, i0, dense, tid);
+        window<false, kDense>(sh, w0, min(bt_last + 1, w0 + kWin), nq, pos0, i0, tid);
         __syncthreads();   // mask, lists and LDS are reused by the next window
       }
     }
@@ -734,21 +757,25 @@ struct Attn {
   }
 };
 
-template <bool kMulti>
+template <bool kMulti, bool kDense>
 __global__ __launch_bounds__(kThreads) void attn_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) AttnLds sh;
   Attn st(a);
-  st.run<kMulti>(sh);
+  st.run<kMulti, kDense>(sh);
 }
 
 }  // namespace
 
 hipError_t launch_attention(const AttnArgs& a, int max_seqlen_q, hipStream_t st) {
   dim3 grid((max_seqlen_q + kTileTok - 1) / kTileTok, a.h_kv, a.batch);
-  if (a.vt_ld <= (int64_t)kWin * kBlock)
-    hipLaunchKernelGGL(attn_kernel<false>, grid, dim3(kThreads), 0, st, a);
-  else
-    hipLaunchKernelGGL(attn_kernel<true>, grid, dim3(kThreads), 0, st, a);
+  const bool multi = a.vt_ld > (int64_t)kWin * kBlock, dense = a.bidx == nullptr;
+  if (dense) {
+    if (multi) hipLaunchKernelGGL((attn_kernel<true, true>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<false, true>), grid, dim3(kThreads), 0, st, a);
+  } else {
+    if (multi) hipLaunchKernelGGL((attn_kernel<true, false>), grid, dim3(kThreads), 0, st, a);
+    else hipLaunchKernelGGL((attn_kernel<false, false>), grid, dim3(kThreads), 0, st, a);
+  }
   return hipGetLastError();
 }
 
