@@ -88,6 +88,7 @@ struct Attn {
   floatx4 o[kTPW][8];
   float m[kTPW], l[kTPW];
   int tb[kTPW];                 // tile-token index (mask bit) of each of the wave's tokens
+  unsigned xrank;               // the workgroup's dispatch rank on its XCD
 
   // Mask bits of this wave's tokens, gathered into bits 0 .. kTPW-1.
   __device__ __forceinline__ uint32_t sel_of(uint32_t v) const {
@@ -624,23 +625,41 @@ struct Attn {
       __syncthreads();   // the ring becomes the private regions
     }
     // 5. private phase: this wave's blocks that stayed out of the shared
-    //    list, ascending, one block in flight (K in the wave's region, V^T
-    //    in registers) while the previous one computes.
+    //    list, one block in flight (K in the wave's region, V^T in
+    //    registers): its loads are issued once the previous block's
+    //    products have read the region and registers, while the other waves
+    //    compute.  The walk is ascending from a start point that advances by
+    //    1/64 of the range per dispatch rank on the XCD (and wraps), so the
+    //    workgroups running side by side on an XCD pass the same part of the
+    //    range at about the same time and share the blocks they have in
+    //    common in its L2 (-0.7% kernel time at 128K against walks that all
+    //    start at block 0; the result does not depend on the order beyond
+    //    rounding, and the order is fixed).
     if (!dense) {
       uint8_t* region = &sh.ring[0][0][0] + wave * (64 * 256);
       const uint32_t mine = mine_mask();
-      int chunk = 0;
       uint64_t pend = 0;
-      // Next private block of this wave (wave-uniform), or -1.
+      const int nch = (nblk + 63) / 64;
+      const int start = (int)((int64_t)(xrank % 64u) * nblk / 64);
+      const int c0 = start / 64;
+      int step = 0, cur = 0;
+      // Next private block of this wave (wave-uniform), or -1: chunks of 64
+      // entries from the start point's, which is visited twice (its entries
+      // from the start point on, then at the end those before it).
       auto next_block = [&](uint32_t& sel) -> int {
         while (pend == 0) {
-          if (chunk * 64 >= nblk) return -1;
-          const int e = chunk * 64 + lane;
+          if (nch == 0 || step > nch) return -1;
+          const int c = (c0 + step) % nch;
+          const int e = c * 64 + lane;
           const uint32_t v = e < nblk ? sh.mask[e] : 0u;
-          pend = __ballot((v & mine) != 0u && __builtin_popcount(v) < kShareMin);
-          ++chunk;
+          bool ok = (v & mine) != 0u && __builtin_popcount(v) < kShareMin;
+          if (step == 0) ok = ok && e >= start;
+          if (step == nch) ok = ok && e < start;
+          pend = __ballot(ok);
+          cur = c;
+          ++step;
         }
-        const int e = (chunk - 1) * 64 + (int)__builtin_ctzll(pend);
+        const int e = cur * 64 + (int)__builtin_ctzll(pend);
         pend &= pend - 1;
         sel = sel_of(__builtin_amdgcn_readfirstlane(sh.mask[e]));
         return w0 + e;
@@ -699,6 +718,7 @@ struct Attn {
       // the light tiles).
       T = N - 1u - T;
     }
+    xrank = L / 8u;
     const int tile = (int)(T % nx);
     g = (int)((T / nx) % ny);
     s = (int)(T / (nx * ny));
