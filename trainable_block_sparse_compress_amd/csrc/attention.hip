@@ -219,6 +219,8 @@ struct Attn {
   uint32_t klo[2];         // K staging: lane byte offset in a 4-row part, per swizzle variant
   uint32_t vlo_stage;      // V^T staging: lane byte offset in an 8-dim part
   uint32_t vlo_frag;       // V^T fragment loads: lane byte offset (dim c16, keys 8*q4)
+  // v as a wave-uniform value, so that the descriptors and offsets derived
+  // from it are formed in scalar registers.
   static __device__ __forceinline__ int64_t uniform64(int64_t v) {
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
