@@ -150,6 +150,45 @@ def test_dense_attention_long(lib, lengths):
     say(f"  max abs err {worst:.3e}")
 
 
+@pytest.mark.parametrize("lengths,stride", [([5000, 3000], 131072 + 64), ([131072 + 2048 + 37], 0)])
+def test_dense_attention_multi_window(lib, lengths, stride):
+    """The dense instance that walks the keys in windows of 2048 blocks, taken
+    when the transposed V's rows are longer than 131072 columns: short
+    sequences with V passed transposed at a longer stride (one window each),
+    and one sequence past 128K keys (two windows).  Sampled rows, including
+    both sides of the window boundary, against the oracle."""
+    say(f"dense multi-window lengths={lengths} stride={stride}")
+    h_q, h_kv = 32, 2
+    inp = D.make_prefill(31, lengths, h_q, h_kv)
+    q, k, v = to_dev(inp.q), to_dev(inp.k), to_dev(inp.v)
+    st = _starts(lengths)
+    out = torch.empty_like(q)
+    lse = torch.empty((h_q, q.shape[0]), dtype=torch.float32, device="cuda")
+    if stride:
+        vt = torch.zeros((h_kv, 128, len(lengths), stride), dtype=torch.bfloat16, device="cuda")
+        for s, n in enumerate(lengths):
+            vt[:, :, s, :n] = v[st[s]:st[s] + n].permute(1, 2, 0)
+        cu = torch.tensor(st + [sum(lengths)], dtype=torch.int32, device="cuda")
+        B.dense_attn(q, k, vt, cu, None, cu, None, len(lengths), max(lengths), max(lengths),
+                     1 / math.sqrt(128), out, lse, v_seq_stride=stride)
+    else:
+        P.DensePlan(st, lengths, st, lengths, sum(lengths), h_q, h_kv, P.SparseConfig()).run(q, k, v, out, lse)
+    torch.cuda.synchronize()
+    of, lf = to_f64(out), lse.cpu().numpy()
+    worst = 0.0
+    for s, n in enumerate(lengths):
+        Ks, Vs = R.as_f64(inp.k[st[s]:st[s] + n]), R.as_f64(inp.v[st[s]:st[s] + n])
+        must = (15, 16, n - 1) if n <= 131072 else (131071, 131072, 131072 + 100, n - 1)
+        pos = sample_positions(n, 16 if n <= 131072 else 3, seed=40 + s, must=must)
+        ref = R.dense_prefill(inp.q[st[s]:st[s] + n], Ks, Vs, h_q // h_kv, 1 / math.sqrt(128), positions=pos)
+        for t in pos:
+            ma, rr = attn_errors(of[st[s] + t], ref[t][0])
+            worst = max(worst, ma)
+            assert ma <= ATT_MAX_ABS and rr <= ATT_REL_RMS, (s, t, ma, rr)
+            assert np.abs(lf[:, st[s] + t] - ref[t][1]).max() < 1e-3, (s, t)
+    say(f"  max abs err {worst:.3e}")
+
+
 # ----------------------------------------------------------------------------
 # sparse attention on given block lists (selection noise excluded)
 # ----------------------------------------------------------------------------
